@@ -1,0 +1,45 @@
+"""Build libar.so: the HIP sources under csrc/ compiled for gfx950 with hipcc.
+
+Flags: -O3 for gfx950 only; packed-fp32 instructions disabled on the device
+pass (the host pass warns that it does not know the feature, which is
+harmless); no fast-math and no denormal flushing, so binary32 adds keep IEEE
+semantics (round to nearest even, subnormals preserved).
+"""
+from __future__ import annotations
+
+import pathlib
+import subprocess
+
+PKG = pathlib.Path(__file__).resolve().parent
+ROOT = PKG.parent
+CSRC = PKG / "csrc"
+LIB = PKG / "libar.so"
+SOURCES = ["host.hip", "reduce.hip", "packet.hip"]
+
+HIPCC_FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-Wall", "-Wextra",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-gpu-flush-denormals-to-zero",
+]
+
+
+def build(verbose: bool = False) -> pathlib.Path:
+    tmp = LIB.with_suffix(".so.tmp")
+    cmd = ["hipcc", *HIPCC_FLAGS, f"-I{ROOT / 'include'}", f"-I{CSRC}",
+           *[str(CSRC / s) for s in SOURCES], "-o", str(tmp)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature for this target"
+    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    tmp.replace(LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,144 @@
+// device.h -- gfx950 device helpers shared by the reduce and packet kernels.
+//
+// bf16 <-> binary32, the rank-order reduction of 16-byte vectors, and the
+// agent-scope 8-byte packet words.  Written for CDNA4: 64-lane wavefronts,
+// 16-byte global loads/stores (global_load_dwordx4), one L2 per XCD.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ar {
+
+// 16-byte vector of eight bf16 (four u32 words, element 2k in the low half
+// of word k).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- bf16 <-> binary32 ----------------------------------------------------
+
+// Low / high bf16 of a 32-bit word widened to binary32.  Exact: the bf16 bits
+// are the upper 16 bits of the binary32 encoding.
+__device__ __forceinline__ float lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// binary32 -> bf16 bits (in the low 16 bits), round to nearest even.
+// Adding 0x7FFF plus the lowest kept bit carries into the kept part exactly
+// when the dropped half is above the midpoint, or at it with an odd kept
+// part; a carry out of the mantissa gives the next binade (or Inf).  NaN is
+// the quiet NaN 0x7FC0.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0x7FC0u : r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Rank-order sum of one 32-bit word (two bf16) over P sources.
+template <int P>
+__device__ __forceinline__ uint32_t reduce_word(const uint32_t (&w)[P]) {
+    float lo = lo_f32(w[0]);
+    float hi = hi_f32(w[0]);
+#pragma unroll
+    for (int p = 1; p < P; ++p) {
+        lo = lo + lo_f32(w[p]);
+        hi = hi + hi_f32(w[p]);
+    }
+    return pack_bf16x2(lo, hi);
+}
+
+// Rank-order sum of eight bf16 (one 16-byte vector) over P sources.
+template <int P>
+__device__ __forceinline__ u32x4 reduce_vec(const u32x4 (&x)[P]) {
+    u32x4 r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        uint32_t w[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) w[p] = x[p][k];
+        r[k] = reduce_word<P>(w);
+    }
+    return r;
+}
+
+// Rank-order sum of one bf16 over P sources (scalar path).
+template <int P>
+__device__ __forceinline__ uint16_t reduce_elem(const uint16_t (&e)[P]) {
+    float acc = __uint_as_float((uint32_t)e[0] << 16);
+#pragma unroll
+    for (int p = 1; p < P; ++p) acc = acc + __uint_as_float((uint32_t)e[p] << 16);
+    return (uint16_t)bf16_rne(acc);
+}
+
+// ---- plain 16-byte vector I/O ---------------------------------------------
+
+__device__ __forceinline__ u32x4 load_vec(const void *base, int64_t elem) {
+    return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem);
+}
+
+__device__ __forceinline__ void store_vec(void *base, int64_t elem, u32x4 v) {
+    *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + elem) = v;
+}
+
+// ---- packet words -----------------------------------------------------------
+//
+// A packet word is the 8-byte half {data: two bf16, flag: u32} of an LL
+// packet, flag in the upper 32 bits (little-endian: bytes 4..7).  Writers
+// and readers run on different XCDs, each with its own L2, so both sides use
+// agent-scope relaxed atomics: the compiler emits global_store_dwordx2 /
+// global_load_dwordx2 with the sc1 (device coherence) bit, which writes
+// through to and reads from the device coherence point instead of a possibly
+// stale per-XCD L2 line.  No fence is needed: data and flag of a word are
+// one single-copy-atomic access, so seeing the flag means seeing the data.
+
+__device__ __forceinline__ uint64_t make_word(uint32_t data, uint32_t flag) {
+    return (uint64_t)data | ((uint64_t)flag << 32);
+}
+
+__device__ __forceinline__ void store_word(uint64_t *p, uint64_t w) {
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t load_word(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t word_flag(uint64_t w) { return (uint32_t)(w >> 32); }
+__device__ __forceinline__ uint32_t word_data(uint64_t w) { return (uint32_t)w; }
+
+// Status word of the control block: agent-scope so every XCD sees it.
+__device__ __forceinline__ int32_t load_status(const int32_t *s) {
+    return __hip_atomic_load(const_cast<int32_t *>(s), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void raise_status(int32_t *s, int32_t code) {
+    int32_t expected = 0;
+    __hip_atomic_compare_exchange_strong(s, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll one packet word until its flag equals `flag`.  Bounded: after
+// `max_spins` polls (or once another waiter has raised the status) it gives
+// up, raises AR_ETIMEDOUT (-4) in the status word and returns false.
+__device__ __forceinline__ bool wait_word(const uint64_t *p, uint32_t flag, uint64_t &w,
+                                          int32_t *status, uint64_t max_spins) {
+    w = load_word(p);
+    uint64_t spins = 0;
+    while (word_flag(w) != flag) {
+        ++spins;
+        if ((spins & 63u) == 0 && load_status(status) != 0) return false;
+        if (spins >= max_spins) {
+            raise_status(status, -4);
+            return false;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        w = load_word(p);
+    }
+    return true;
+}
+
+}  // namespace ar

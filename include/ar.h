@@ -1,0 +1,215 @@
+/*
+ * ar.h -- C ABI of libar.so: one rank's share of a small-message bf16
+ * allreduce with fp32 accumulation, on AMD Instinct MI355X (gfx950).
+ *
+ * All P "peer" buffers live in the calling GPU's own HBM: the library runs the
+ * share of one rank, or of several emulated ranks, on a single device.
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ *  - Element type: bf16, passed as raw 16-bit patterns.  Element pointers must
+ *    be 2-byte aligned; any further misalignment is allowed and takes a
+ *    slower path (16-byte vectors are used where every pointer of a call
+ *    shares one alignment, scalar accesses for the rest).
+ *  - Arithmetic: element i of the result is the binary32 sum
+ *    ((x_0[i] + x_1[i]) + x_2[i]) + ... + x_{P-1}[i], in rank order, each
+ *    bf16 widened exactly, IEEE round-to-nearest-even adds with subnormals
+ *    kept, then rounded to bf16 with round-to-nearest-even.  Any NaN result
+ *    is stored as the quiet NaN 0x7FC0.  Results are bit-exact and identical
+ *    for every output and every rank.
+ *  - Pointers: device pointers (hipMalloc or torch CUDA tensors).  Arrays of
+ *    P peer buffers are passed BY VALUE in an ar_ptrs struct, which the
+ *    library copies into the kernel's arguments: no device-side pointer table
+ *    and no extra launch to build one (Helion PR #245 "One shot all reduce
+ *    Example", review thread on launching an extra kernel to turn a pointer
+ *    array into a tensor versus passing pointers as kernel arguments).
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *    stream).  Every call is asynchronous on that stream: the library never
+ *    allocates, never synchronises and keeps no pointer after it returns.
+ *    The caller owns and allocates every buffer.
+ *  - Errors: argument errors are detected on the host before anything is
+ *    launched and returned as a negative AR_E* code; a failed launch returns
+ *    AR_ELAUNCH.  Errors found while the kernel runs (a bounded wait that ran
+ *    out) are reported through the device control block (ar_ctrl).
+ *  - n == 0 is a successful no-op.
+ */
+#ifndef AR_H
+#define AR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_MAX_P 8
+
+/* P device pointers (entries >= P are ignored), passed by value. */
+typedef struct ar_ptrs {
+    void *p[AR_MAX_P];
+} ar_ptrs;
+
+enum ar_status {
+    AR_OK = 0,
+    AR_EINVAL = -1,    /* bad argument: P, n, rank, flag, null or misaligned pointer */
+    AR_EALIAS = -2,    /* buffers overlap where the call forbids it */
+    AR_ELAUNCH = -3,   /* the HIP launch (or a device query it needs) failed */
+    AR_ETIMEDOUT = -4  /* device side: a bounded wait for a packet ran out */
+};
+
+/*
+ * Device control block of the packet kernels: 64 bytes of device memory the
+ * caller allocates and zeroes once.  `status` is AR_OK until a kernel's
+ * bounded wait runs out; the first waiter to time out stores AR_ETIMEDOUT and
+ * every waiter of that launch then stops waiting.  The library never clears
+ * it: the caller reads it back (e.g. after synchronising) and re-zeroes it.
+ */
+#define AR_CTRL_BYTES 64
+typedef struct ar_ctrl {
+    int32_t status;
+    uint32_t reserved[15];
+} ar_ctrl;
+
+/* Default bound on the polls of one packet word (0 passed as max_spins). */
+#define AR_DEFAULT_MAX_SPINS (1ull << 22)
+
+/* ---------------------------------------------------------------------------
+ * ar_oneshot_sum -- one-shot allreduce share: out[i] = sum_r in.p[r][i].
+ *
+ * Every rank is owed the whole buffer and keeps the whole result: the
+ * allreduce case of the one-shot push-reduce kernel (torchcomms PR #3850
+ * "Add HIP-graph capture coverage for the sharded-relay collectives", commit
+ * summary D117629707, srcStride = 0 and ownOffset = 0); the same one-shot sum
+ * as Helion PR #245 "One shot all reduce Example".
+ *   in   P input buffers of n bf16 each (read only).
+ *   out  one output buffer of n bf16.  It may be identical to one of the
+ *        inputs (in place); any other overlap with an input is AR_EALIAS.
+ *   P    2..8.
+ * ------------------------------------------------------------------------- */
+int ar_oneshot_sum(ar_ptrs in, void *out, int P, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * ar_oneshot_write_bcast -- write mode: the reduced vector is stored straight
+ * into all P output buffers, whose pointers reach the kernel by value
+ * (aiter PR #1910 "optimize allreduce write mode by broadcast output ptr",
+ * Motivation: stage 2 writes directly into the other ranks' outputs; Technical
+ * Details: the output pointers are broadcast on the host).
+ *   in   P input buffers of n bf16.
+ *   out  P output buffers of n bf16; all P receive identical data.  out.p[k]
+ *        may equal in.p[k'] exactly (in place); partial overlaps between any
+ *        two buffers are AR_EALIAS.
+ * ------------------------------------------------------------------------- */
+int ar_oneshot_write_bcast(ar_ptrs in, ar_ptrs out, int P, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * ar_twoshot_share -- rank `rank`'s two-shot share: reduce its slice over the
+ * P inputs and write that slice into all P outputs (reduce-scatter stage, then
+ * the write-mode broadcast of aiter PR #1910, Motivation).  Slices: L =
+ * floor(n / (128 P)) * 128; rank r owns [r L, (r+1) L), the last rank owns
+ * [(P-1) L, n), so every slice boundary is 128-element aligned and the last
+ * slice absorbs the remainder (torchcomms PR #3850, commit summary
+ * D117629683).  Outputs outside the slice are not touched.
+ *   in, out, P as for ar_oneshot_write_bcast; rank in [0, P).
+ * ------------------------------------------------------------------------- */
+int ar_twoshot_share(ar_ptrs in, ar_ptrs out, int P, int rank, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * LL packets.  Data and flag travel in one packet so that arrival is read off
+ * the data itself (ARK PR #254 "Add monolithic fused packet allreduce kernel
+ * and Model::all_reduce_packet API", description).  Layout of packet k
+ * (16 bytes, 16-byte aligned, four little-endian u32 words):
+ *     word 0 = elem[4k]   | elem[4k+1] << 16      (data0)
+ *     word 1 = flag                               (flag0)
+ *     word 2 = elem[4k+2] | elem[4k+3] << 16      (data1)
+ *     word 3 = flag                               (flag1)
+ * Elements past n are encoded as 0.  Each 8-byte half {data, flag} is written
+ * and read as one agent-scope atomic, so a reader that sees the expected flag
+ * in a half also sees that half's data.  A packet counts as arrived only when
+ * both flags equal the expected value; flags are never cleared, so a packet
+ * left by an earlier call (older flag) reads as not yet arrived (torchcomms
+ * PR #3850, commit summary D117629704: flags never cleared, stale flags
+ * compare as not arrived).
+ * ------------------------------------------------------------------------- */
+
+/* Number of packets for n elements: ceil(n / 4). */
+int64_t ar_ll_packets(int64_t n);
+
+/* Encode n bf16 from `src` into ceil(n/4) packets at `dst_pkts` (16-byte
+ * aligned) with flag `flag` (!= 0).  src and dst must not overlap. */
+int ar_ll_encode(const void *src, void *dst_pkts, int64_t n, uint32_t flag, void *stream);
+
+/* Wait until every packet at `src_pkts` carries `flag` in both flag words,
+ * then decode n bf16 into `dst`.  Each packet word is polled at most
+ * `max_spins` times (0 = AR_DEFAULT_MAX_SPINS); on timeout AR_ETIMEDOUT is
+ * stored in ctrl->status and dst is undefined.  `ctrl` is required. */
+int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void *ctrl,
+                 uint64_t max_spins, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * ar_packet_fused -- fused LL-packet allreduce for emulated ranks
+ * [rank_lo, rank_hi) of P, in ONE launch: scatter, reduce and broadcast are
+ * fused into one kernel and synchronised only by the flags inside the packets,
+ * not by barriers between workgroups (ARK PR #254, description; a rotating
+ * per-call flag, which that page lists as deferred under Known limitations).
+ *
+ * Each rank j owns the two-shot slice j (same rule as ar_twoshot_share) and a
+ * scratch buffer scratch.p[j] of ar_packet_scratch_bytes(P, n) bytes laid out
+ * as [inbox: P slots][resbox: P slots], each slot S = ar_packet_slot_packets
+ * (P, n) packets (sized for the largest, i.e. last, slice).  Rank r:
+ *   scatter    encodes in.p[r][slice j] into inbox_j[slot r], for every j;
+ *   reduce     polls inbox_r[slot 0..P-1], decodes, sums in rank order;
+ *   broadcast  encodes the reduced slice into resbox_j[slot r], for every j;
+ *   receive    polls resbox_r[slot 0..P-1] and decodes into out.p[r].
+ * Packets past a slice's length are never written.
+ *   in       P inputs of n bf16 (all P are read by the ranks in the range).
+ *   scratch  P scratch buffers, 16-byte aligned; zero them once before the
+ *            first call; the library never clears them.
+ *   out      P outputs of n bf16; out.p[r] is written for r in the range.
+ *   flag     != 0, strictly increasing from call to call on one scratch set
+ *            (call c uses flag c + 1).  Wrap-around is not supported.
+ *   ctrl     control block (AR_CTRL_BYTES), required.
+ * A range covering fewer than all P ranks only completes if the packets of
+ * the other ranks for this flag are already in place (e.g. staged with
+ * ar_ll_encode); otherwise it times out and reports AR_ETIMEDOUT.  Inputs,
+ * outputs and scratch buffers must not overlap each other (AR_EALIAS).  Two
+ * calls in flight on one scratch set are not allowed.
+ * ------------------------------------------------------------------------- */
+int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo, int rank_hi,
+                    int64_t n, uint32_t flag, void *ctrl, uint64_t max_spins, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Host-only helpers: no GPU needed, no HIP call made.
+ * ------------------------------------------------------------------------- */
+
+/* Slice [*begin, *end) of `rank` under the two-shot rule above. */
+int ar_slice_range(int P, int rank, int64_t n, int64_t *begin, int64_t *end);
+
+/* Packets per scratch slot (ceil of the last slice's length / 4), or < 0. */
+int64_t ar_packet_slot_packets(int P, int64_t n);
+
+/* Bytes of one rank's scratch buffer: 2 * P * slot_packets * 16, or < 0. */
+int64_t ar_packet_scratch_bytes(int P, int64_t n);
+
+/* Static, human-readable name of a status code. */
+const char *ar_strerror(int code);
+
+/* ---------------------------------------------------------------------------
+ * Measurement helper: launch an empty kernel on `stream`.  Gives the dispatch
+ * floor that latency-bound calls are compared against.
+ * ------------------------------------------------------------------------- */
+int ar_noop(void *stream);
+
+/* Benchmark-only launch-shape overrides (process-global, not thread-safe).
+ * ar_set_reduce_tuning: unroll (vectors in flight per lane) in {0 = automatic,
+ * 1, 2, 4} and a cap on workgroups (0 = automatic) for ar_oneshot_sum,
+ * ar_oneshot_write_bcast and ar_twoshot_share.  ar_set_packet_tuning:
+ * workgroups per emulated rank of ar_packet_fused (0 = automatic; never more
+ * than fit on the device at once).  Results do not depend on either. */
+int ar_set_reduce_tuning(int unroll, int max_blocks);
+int ar_set_packet_tuning(int per_rank);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AR_H */

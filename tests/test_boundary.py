@@ -1,0 +1,187 @@
+"""CPU tests of the C ABI: it loads, exports every declared symbol, and its
+host-only helpers and argument checks behave as include/ar.h states.  No
+compute call reaches a GPU here: every call either is host-only or fails
+validation (or is an n == 0 no-op) before anything is launched."""
+from __future__ import annotations
+
+import ctypes
+import pathlib
+import re
+
+import pytest
+
+from allreduce_reduction_way_amd import ar
+from oracle import oracle as O
+
+ROOT = pathlib.Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "ar.h"
+GOLDEN = pathlib.Path(__file__).resolve().parent / "golden"
+
+FAKE = 0x7F0000000000  # a 256-byte aligned address that is never dereferenced here
+STREAM = 0
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", HEADER.read_text(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(ar_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for must in ["ar_oneshot_sum", "ar_oneshot_write_bcast", "ar_twoshot_share", "ar_ll_encode",
+                 "ar_ll_decode", "ar_packet_fused", "ar_slice_range", "ar_packet_scratch_bytes"]:
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(str(ar.LIB_PATH))
+    missing = [n for n in _declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_declared_symbol():
+    assert all(callable(getattr(ar, n, None)) for n in _declared_functions())
+
+
+# ----------------------------------------------------------- host-only helpers
+
+def _slice_rows():
+    for raw in (GOLDEN / "slices.txt").read_text().splitlines():
+        line = raw.split("#", 1)[0].strip()
+        if line:
+            yield tuple(int(t) for t in line.split())
+
+
+@pytest.mark.parametrize("P,n,r,b,e", list(_slice_rows()))
+def test_slice_range_matches_golden_table(P, n, r, b, e):
+    if P < 2:
+        pytest.skip("the library takes P >= 2")
+    assert ar.ar_slice_range(P, r, n) == (b, e)
+
+
+@pytest.mark.parametrize("P", range(2, 9))
+@pytest.mark.parametrize("n", [0, 1, 5, 1023, 1024, 1025, 4096, 3481600, 3670016, 2252800])
+def test_slice_and_scratch_helpers_agree_with_oracle(P, n):
+    for r in range(P):
+        assert ar.ar_slice_range(P, r, n) == O.slice_range(P, n, r)
+    assert ar.ar_packet_slot_packets(P, n) == O.packet_slot_packets(P, n)
+    assert ar.ar_packet_scratch_bytes(P, n) == O.packet_scratch_bytes(P, n)
+
+
+def test_ll_packets():
+    assert [ar.ar_ll_packets(n) for n in (0, 1, 4, 5, 8)] == [0, 1, 1, 2, 2]
+
+
+def test_strerror_names_every_code():
+    for code, name in [(0, "AR_OK"), (-1, "AR_EINVAL"), (-2, "AR_EALIAS"), (-3, "AR_ELAUNCH"),
+                       (-4, "AR_ETIMEDOUT")]:
+        assert ar.ar_strerror(code).startswith(name)
+
+
+# ------------------------------------------------- validation before any launch
+
+def _err(fn, *args, **kw):
+    with pytest.raises(ar.ArError) as ei:
+        fn(*args, **kw)
+    return ei.value.code
+
+
+def _bufs(P, stride=1 << 24, base=FAKE):
+    return [base + k * stride for k in range(P)]
+
+
+@pytest.mark.parametrize("P", [-1, 0, 1, 9])
+def test_bad_P(P):
+    L = ar.lib()
+    ins, outs = ar._ptrs(_bufs(8)), ar._ptrs(_bufs(8, base=FAKE + (1 << 30)))
+    assert L.ar_oneshot_sum(ins, FAKE + (1 << 31), P, 16, STREAM) == ar.AR_EINVAL
+    assert L.ar_oneshot_write_bcast(ins, outs, P, 16, STREAM) == ar.AR_EINVAL
+    assert L.ar_twoshot_share(ins, outs, P, 0, 4096, STREAM) == ar.AR_EINVAL
+    assert L.ar_packet_fused(ins, ar._ptrs(_bufs(8, base=FAKE + (1 << 32))), outs, P, 0, 1, 4096,
+                             1, FAKE + (3 << 30), 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_packet_scratch_bytes(P, 4096) < 0
+
+
+def test_negative_n_and_null_and_odd_pointers():
+    ins = _bufs(8)
+    out = FAKE + (1 << 30)
+    assert _err(ar.ar_oneshot_sum, ins, out, n=-1, stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_oneshot_sum, ins[:7] + [0], out, n=16, stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_oneshot_sum, ins, out + 1, n=16, stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_oneshot_write_bcast, ins, _bufs(8, base=out)[:7] + [0], n=16,
+                stream=STREAM) == ar.AR_EINVAL
+
+
+def test_zero_length_is_a_noop():
+    ar.ar_oneshot_sum(_bufs(8), FAKE + (1 << 30), n=0, stream=STREAM)
+    ar.ar_oneshot_write_bcast(_bufs(8), _bufs(8, base=FAKE + (1 << 30)), n=0, stream=STREAM)
+    ar.ar_twoshot_share(_bufs(8), _bufs(8, base=FAKE + (1 << 30)), 3, n=0, stream=STREAM)
+
+
+def test_partial_overlap_is_an_alias_but_exact_in_place_is_not_rejected():
+    ins = _bufs(8)
+    # output starting 2 elements into input 3: partial overlap
+    assert _err(ar.ar_oneshot_sum, ins, ins[3] + 4, n=64, stream=STREAM) == ar.AR_EALIAS
+    outs = _bufs(8, base=FAKE + (1 << 30))
+    outs[5] = outs[4] + 32  # two outputs overlapping partially
+    assert _err(ar.ar_oneshot_write_bcast, ins, outs, n=64, stream=STREAM) == ar.AR_EALIAS
+
+
+def test_twoshot_rank_out_of_range():
+    ins, outs = _bufs(8), _bufs(8, base=FAKE + (1 << 30))
+    for rank in (-1, 8):
+        assert _err(ar.ar_twoshot_share, ins, outs, rank, n=4096, stream=STREAM) == ar.AR_EINVAL
+
+
+def test_twoshot_alias_checked_on_the_slice():
+    P, n, rank = 8, 8192, 4          # L = 1024: rank 4 owns elements [4096, 5120)
+    ins = _bufs(P)
+    outs = _bufs(P, base=FAKE + (1 << 30))
+    outs[2] = ins[2] + 2 * 8         # output 2 shifted 8 elements into input 2: in-slice overlap
+    assert _err(ar.ar_twoshot_share, ins, outs, rank, n=n, stream=STREAM) == ar.AR_EALIAS
+
+
+def test_packet_validation():
+    P, n = 8, 4096
+    ins = _bufs(P)
+    outs = _bufs(P, base=FAKE + (1 << 30))
+    scr = _bufs(P, base=FAKE + (1 << 31))
+    ctrl = FAKE + (3 << 30)
+    kw = dict(n=n, stream=STREAM)
+    assert _err(ar.ar_packet_fused, ins, scr, outs, 0, ctrl, **kw) == ar.AR_EINVAL       # flag 0
+    assert _err(ar.ar_packet_fused, ins, scr, outs, 1, 0, **kw) == ar.AR_EINVAL          # no ctrl
+    assert _err(ar.ar_packet_fused, ins, scr, outs, 1, ctrl, rank_lo=3, rank_hi=3,
+                **kw) == ar.AR_EINVAL                                                     # empty
+    assert _err(ar.ar_packet_fused, ins, scr, outs, 1, ctrl, rank_lo=0, rank_hi=9,
+                **kw) == ar.AR_EINVAL
+    bad_scr = list(scr)
+    bad_scr[1] += 8                                                                       # not 16-B
+    assert _err(ar.ar_packet_fused, ins, bad_scr, outs, 1, ctrl, **kw) == ar.AR_EINVAL
+    alias_out = list(outs)
+    alias_out[0] = ins[0]                                                                 # in place
+    assert _err(ar.ar_packet_fused, ins, scr, alias_out, 1, ctrl, **kw) == ar.AR_EALIAS
+    alias_scr = list(scr)
+    alias_scr[3] = scr[2] + 4096                                                          # overlap
+    assert _err(ar.ar_packet_fused, ins, alias_scr, outs, 1, ctrl, **kw) == ar.AR_EALIAS
+    assert _err(ar.ar_packet_fused, ins, scr, outs, 1, scr[0] + 64, **kw) == ar.AR_EALIAS
+    ar.ar_packet_fused(ins, scr, outs, 1, ctrl, n=0, stream=STREAM)                        # no-op
+
+
+def test_codec_validation():
+    src, pk, ctrl = FAKE, FAKE + (1 << 30), FAKE + (1 << 31)
+    assert _err(ar.ar_ll_encode, src, pk, 0, n=16, stream=STREAM) == ar.AR_EINVAL       # flag 0
+    assert _err(ar.ar_ll_encode, src, pk + 8, 1, n=16, stream=STREAM) == ar.AR_EINVAL   # 16-B
+    assert _err(ar.ar_ll_encode, src, src + 16, 1, n=16, stream=STREAM) == ar.AR_EALIAS
+    assert _err(ar.ar_ll_decode, pk, src, 1, 0, n=16, stream=STREAM) == ar.AR_EINVAL    # ctrl
+    assert _err(ar.ar_ll_decode, pk, src, 1, pk + 16, n=16, stream=STREAM) == ar.AR_EALIAS
+    ar.ar_ll_encode(src, pk, 1, n=0, stream=STREAM)
+    ar.ar_ll_decode(pk, src, 1, ctrl, n=0, stream=STREAM)
+
+
+def test_tuning_validation():
+    assert _err(ar.ar_set_reduce_tuning, 3, 0) == ar.AR_EINVAL
+    assert _err(ar.ar_set_reduce_tuning, 1, -1) == ar.AR_EINVAL
+    assert _err(ar.ar_set_packet_tuning, -1) == ar.AR_EINVAL
+    ar.ar_set_reduce_tuning(0, 0)
+    ar.ar_set_packet_tuning(0)

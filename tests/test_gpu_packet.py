@@ -1,0 +1,233 @@
+"""GPU parity of the LL-packet codec and the fused packet share against the
+CPU oracle: outputs bit-exact, and the scratch images (every packet word and
+flag) byte-exact after each call of a flag-rotating sequence.  Waits that
+must fail are forced from the host (a stale flag plus a small spin bound), so
+every kernel still exits on its own."""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from allreduce_reduction_way_amd import ar, inputs as I, workloads as W
+from gpu_util import DEV, Guarded, announce, ctrl_block, ctrl_status, to_dev, to_host
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+SMALL_SPINS = 4096      # bound for waits that are meant to time out
+
+
+def _scratch(P, n, images=None):
+    nbytes = O.packet_scratch_bytes(P, n)
+    if images is None:
+        return [torch.zeros(nbytes, dtype=torch.uint8, device=DEV) for _ in range(P)]
+    return [torch.from_numpy(np.ascontiguousarray(im)).to(DEV) for im in images]
+
+
+def _images(scratch):
+    return [t.cpu().numpy() for t in scratch]
+
+
+# ------------------------------------------------------------------ codec
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8, 63, 64, 65, 1000, 4096 * 9 + 3])
+def test_ll_encode_bytes_match_oracle(n):
+    rng = np.random.default_rng(n)
+    y = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+    f = 0x11223344 + n
+    pk = torch.zeros(16 * O.ll_packets(n) + 64, dtype=torch.uint8, device=DEV)
+    announce(f"ll_encode n={n}")
+    ar.ar_ll_encode(to_dev(y), pk, f)
+    torch.cuda.synchronize()
+    got = pk.cpu().numpy()
+    assert got[16 * O.ll_packets(n):].sum() == 0          # nothing past the last packet
+    assert np.array_equal(got[: 16 * O.ll_packets(n)].view(np.uint32), O.ll_encode(y, f))
+
+
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 999, 4096 * 9 + 3])
+@pytest.mark.parametrize("shift", [0, 1])
+def test_ll_decode_of_oracle_packets(n, shift):
+    rng = np.random.default_rng(n + 7)
+    y = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+    f = 9
+    pk = to_dev(O.ll_encode(y, f).view(np.uint16))
+    out = Guarded(n, shift=shift)
+    ctrl = ctrl_block()
+    announce(f"ll_decode n={n} shift={shift}")
+    ar.ar_ll_decode(pk, out.view, f, ctrl)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == 0
+    assert np.array_equal(out.host(), y) and out.guards_intact()
+
+
+def test_ll_round_trip_on_device_and_stale_flag_times_out():
+    n = 50001
+    y = I.uniform_bf16(n, 0, 0)
+    pk = torch.zeros(16 * O.ll_packets(n), dtype=torch.uint8, device=DEV)
+    out = Guarded(n)
+    ctrl = ctrl_block()
+    announce("ll round trip flag 5")
+    ar.ar_ll_encode(to_dev(y), pk, 5)
+    ar.ar_ll_decode(pk, out.view, 5, ctrl)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == 0 and np.array_equal(out.host(), y)
+    announce("ll decode of stale packets (flag 5, waiting for 6), small spin bound")
+    ar.ar_ll_decode(pk, out.view, 6, ctrl, max_spins=SMALL_SPINS)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == ar.AR_ETIMEDOUT
+
+
+def test_ll_decode_half_stale_packet_times_out():
+    # one packet whose second flag word is stale: the packet is not arrived
+    n = 4096
+    y = I.uniform_bf16(n, 1, 0)
+    words = O.ll_encode(y, 3)
+    words[4 * 100 + 3] = 2
+    out = Guarded(n)
+    ctrl = ctrl_block()
+    announce("ll decode with one half-stale packet")
+    ar.ar_ll_decode(to_dev(words.view(np.uint16)), out.view, 3, ctrl, max_spins=SMALL_SPINS)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == ar.AR_ETIMEDOUT
+
+
+# ---------------------------------------------------------- fused packet path
+
+@pytest.mark.parametrize("P,n", [(8, 1024 * 3 + 5), (8, 1000), (8, 4096), (2, 513), (3, 777),
+                                 (4, 4096 * 5 + 130), (8, 8192 * 9 + 1)])
+def test_packet_fused_three_calls_match_oracle(P, n):
+    scratch = _scratch(P, n)
+    images = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    ctrl = ctrl_block()
+    for call in range(3):
+        f = call + 1
+        xs = I.make_inputs("uniform", P, n, seed=call)
+        outs = [Guarded(n) for _ in range(P)]
+        announce(f"packet_fused P={P} n={n} call={call} flag={f}")
+        ar.ar_packet_fused([to_dev(x) for x in xs], scratch, [o.view for o in outs], f, ctrl)
+        torch.cuda.synchronize()
+        assert ctrl_status(ctrl) == 0
+        want_outs, images = O.packet_fused(xs, f, images)
+        for r in range(P):
+            assert np.array_equal(outs[r].host(), want_outs[r]), (call, r)
+            assert outs[r].guards_intact()
+        got = _images(scratch)
+        for r in range(P):
+            assert np.array_equal(got[r], images[r]), (call, r)
+
+
+def test_packet_fused_512x7168_p8_workload():
+    w = W.PACKET_512x7168
+    P, n = w.P, w.n
+    scratch = _scratch(P, n)
+    images = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    ctrl = ctrl_block()
+    d_out = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    for call in range(w.calls):
+        f = call + 1
+        xs = I.make_inputs(w.dist, P, n, seed=call)
+        announce(f"{w.name} call={call} flag={f}")
+        ar.ar_packet_fused([to_dev(x) for x in xs], scratch, d_out, f, ctrl)
+        torch.cuda.synchronize()
+        assert ctrl_status(ctrl) == 0
+        want_outs, images = O.packet_fused(xs, f, images)
+        for r in range(P):
+            assert np.array_equal(to_host(d_out[r]), want_outs[r]), (call, r)
+        got = _images(scratch)
+        for r in range(P):
+            assert np.array_equal(got[r], images[r]), (call, r)
+
+
+def _without_rank(images, P, n, rank):
+    """The oracle's images with every packet that `rank` writes zeroed: its
+    slot in every inbox and every resbox."""
+    S = O.packet_slot_packets(P, n)
+    out = []
+    for im in images:
+        im = im.copy()
+        words = im.view(np.uint32).reshape(2 * P, 4 * S)
+        words[rank] = 0
+        words[P + rank] = 0
+        out.append(im)
+    return out
+
+
+@pytest.mark.parametrize("P,n,rank", [(8, 4096 * 3 + 11, 3), (8, 512 * 7168, 3), (4, 777, 0)])
+def test_packet_single_rank_with_staged_peers(P, n, rank):
+    xs = I.make_inputs("uniform", P, n, seed=5)
+    zero = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    want_outs, full = O.packet_fused(xs, 1, zero)
+    scratch = _scratch(P, n, _without_rank(full, P, n, rank))
+    outs = [Guarded(n) for _ in range(P)]
+    ctrl = ctrl_block()
+    announce(f"packet single rank {rank} of P={P} n={n}")
+    ar.ar_packet_fused([to_dev(x) for x in xs], scratch, [o.view for o in outs], 1, ctrl,
+                       rank_lo=rank, rank_hi=rank + 1)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == 0
+    assert np.array_equal(outs[rank].host(), want_outs[rank])
+    for r in range(P):
+        if r != rank:
+            assert (outs[r].host() == 0x5A5A).all()      # other ranks' outputs untouched
+        assert outs[r].guards_intact()
+    got = _images(scratch)
+    for r in range(P):
+        assert np.array_equal(got[r], full[r])
+
+
+def test_packet_single_rank_stale_peers_time_out():
+    # peers staged for flag 1; the call waits for flag 2 -> bounded wait ends
+    P, n, rank = 8, 4096 * 2 + 3, 3
+    xs = I.make_inputs("uniform", P, n, seed=6)
+    zero = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    _, full = O.packet_fused(xs, 1, zero)
+    scratch = _scratch(P, n, full)
+    ctrl = ctrl_block()
+    outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    announce("packet single rank, stale peer packets, small spin bound")
+    ar.ar_packet_fused([to_dev(x) for x in xs], scratch, outs, 2, ctrl, rank_lo=rank,
+                       rank_hi=rank + 1, max_spins=SMALL_SPINS)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == ar.AR_ETIMEDOUT
+
+
+def test_packet_zeroed_scratch_single_rank_times_out():
+    P, n = 4, 2048
+    xs = I.make_inputs("uniform", P, n, seed=8)
+    scratch = _scratch(P, n)
+    ctrl = ctrl_block()
+    outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    announce("packet single rank, no peers at all, small spin bound")
+    ar.ar_packet_fused([to_dev(x) for x in xs], scratch, outs, 1, ctrl, rank_lo=1, rank_hi=2,
+                       max_spins=SMALL_SPINS)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == ar.AR_ETIMEDOUT
+
+
+def test_packet_split_launch_with_skewed_producers():
+    """Ranks 0..3 and 4..7 launched on two streams, the second after a host
+    sleep: the first launch's waits span the skew and complete."""
+    P, n = 8, 8192 * 5 + 9
+    xs = I.make_inputs("uniform", P, n, seed=12)
+    d_in = [to_dev(x) for x in xs]
+    scratch = _scratch(P, n)
+    outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ctrl_a, ctrl_b = ctrl_block(), ctrl_block()
+    s_a, s_b = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    ar.ar_set_packet_tuning(8)       # small grids, so both launches are resident together
+    try:
+        announce("packet split launch: ranks 0..3 now, ranks 4..7 after 50 ms")
+        ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl_a, rank_lo=0, rank_hi=4, stream=s_a)
+        time.sleep(0.05)
+        ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl_b, rank_lo=4, rank_hi=8, stream=s_b)
+        torch.cuda.synchronize()
+    finally:
+        ar.ar_set_packet_tuning(0)
+    assert ctrl_status(ctrl_a) == 0 and ctrl_status(ctrl_b) == 0
+    y = O.oneshot_sum(xs)
+    for t in outs:
+        assert np.array_equal(to_host(t), y)

@@ -1,0 +1,216 @@
+"""GPU parity of the reduce entry points (one-shot, write mode, two-shot)
+against the CPU oracle, element by element and bit-exact: the kernels add in
+rank order like the oracle, so no tolerance is needed."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from allreduce_reduction_way_amd import ar, inputs as I, workloads as W
+from gpu_util import Guarded, announce, to_dev, to_host
+from oracle import oracle as O
+
+pytestmark = pytest.mark.gpu
+
+SIZES = [1, 3, 4, 7, 8, 9, 15, 16, 17, 63, 64, 65, 127, 128, 1023, 1024, 1025, 4095, 4096, 4097,
+         65536 + 7, 100003]
+
+
+def _inputs(P, n, seed=0, kind="uniform"):
+    return I.make_inputs(kind, P, n, seed=seed)
+
+
+def _special_inputs(P, n, seed):
+    """Arbitrary bit patterns: NaN, +-Inf, +-0, subnormals and every exponent."""
+    rng = np.random.default_rng(seed)
+    xs = [rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16) for _ in range(P)]
+    specials = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x0001, 0x8001, 0x007F,
+                         0x7F7F, 0xFF7F], dtype=np.uint16)
+    for x in xs:
+        idx = rng.integers(0, n, max(1, n // 8))
+        x[idx] = specials[rng.integers(0, specials.size, idx.size)]
+    return xs
+
+
+# ------------------------------------------------------------------- one-shot
+
+@pytest.mark.parametrize("P", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("n", SIZES)
+def test_oneshot_sum_matches_oracle(P, n):
+    xs = _inputs(P, n, seed=n % 97)
+    d_in = [to_dev(x) for x in xs]
+    out = Guarded(n)
+    announce(f"oneshot P={P} n={n}")
+    ar.ar_oneshot_sum(d_in, out.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.host(), O.oneshot_sum(xs))
+    assert out.guards_intact()
+
+
+@pytest.mark.parametrize("P", [2, 8])
+@pytest.mark.parametrize("n", [9, 4096 + 5, 100003])
+def test_oneshot_special_values(P, n):
+    xs = _special_inputs(P, n, seed=P * 1000 + n)
+    out = Guarded(n)
+    announce(f"oneshot specials P={P} n={n}")
+    ar.ar_oneshot_sum([to_dev(x) for x in xs], out.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.host(), O.oneshot_sum(xs))
+
+
+@pytest.mark.parametrize("P", [4, 8])
+def test_oneshot_position_fill(P):
+    n = 8192 + 3
+    xs = _inputs(P, n, kind="position")
+    out = Guarded(n)
+    announce(f"oneshot position fill P={P}")
+    ar.ar_oneshot_sum([to_dev(x) for x in xs], out.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.host(), O.oneshot_sum(xs))
+
+
+@pytest.mark.parametrize("shifts", [(1,) * 9, (2,) * 9, (4,) * 9, (7,) * 9,
+                                    (0, 1, 2, 3, 4, 5, 6, 7, 0), (0,) * 8 + (3,)])
+@pytest.mark.parametrize("n", [5, 1000, 4096 + 13])
+def test_oneshot_misaligned_views(shifts, n):
+    """Element shifts of the 8 inputs and the output inside their allocations:
+    equal shifts take the head/vector/tail split, unequal ones the scalar path."""
+    P = 8
+    xs = _inputs(P, n, seed=3)
+    ins = [Guarded(n, shift=shifts[p], init=xs[p]) for p in range(P)]
+    out = Guarded(n, shift=shifts[P])
+    announce(f"oneshot misaligned shifts={shifts} n={n}")
+    ar.ar_oneshot_sum([g.view for g in ins], out.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.host(), O.oneshot_sum(xs))
+    assert out.guards_intact()
+
+
+def test_oneshot_in_place():
+    P, n = 8, 4096 + 77
+    xs = _inputs(P, n, seed=11)
+    d_in = [to_dev(x) for x in xs]
+    announce("oneshot in place")
+    ar.ar_oneshot_sum(d_in, d_in[3])
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(d_in[3]), O.oneshot_sum(xs))
+
+
+def test_oneshot_4096_p8_workload():
+    w = W.ONESHOT_4K
+    xs = I.make_inputs(w.dist, w.P, w.n, seed=0)
+    out = Guarded(w.n)
+    announce(w.name)
+    for _ in range(3):
+        ar.ar_oneshot_sum([to_dev(x) for x in xs], out.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.host(), O.oneshot_sum(xs))
+    assert out.guards_intact()
+
+
+# ----------------------------------------------------------------- write mode
+
+@pytest.mark.parametrize("P", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1023, 1025, 4096, 65536 + 3])
+def test_write_bcast_matches_oracle(P, n):
+    xs = _inputs(P, n, seed=n % 13)
+    outs = [Guarded(n) for _ in range(P)]
+    announce(f"write_bcast P={P} n={n}")
+    ar.ar_oneshot_write_bcast([to_dev(x) for x in xs], [o.view for o in outs])
+    torch.cuda.synchronize()
+    want = O.write_bcast(xs)
+    for o, w_ in zip(outs, want):
+        assert np.array_equal(o.host(), w_)
+        assert o.guards_intact()
+
+
+def test_write_bcast_in_place_every_rank():
+    P, n = 8, 10000
+    xs = _inputs(P, n, seed=21)
+    d = [to_dev(x) for x in xs]
+    announce("write_bcast in place")
+    ar.ar_oneshot_write_bcast(d, d)
+    torch.cuda.synchronize()
+    y = O.oneshot_sum(xs)
+    for t in d:
+        assert np.array_equal(to_host(t), y)
+
+
+def test_write_bcast_misaligned_outputs():
+    P, n = 8, 3001
+    xs = _inputs(P, n, seed=4)
+    ins = [Guarded(n, shift=1, init=x) for x in xs]
+    outs = [Guarded(n, shift=1 + (k % 2)) for k in range(P)]
+    announce("write_bcast misaligned")
+    ar.ar_oneshot_write_bcast([g.view for g in ins], [o.view for o in outs])
+    torch.cuda.synchronize()
+    y = O.oneshot_sum(xs)
+    for o in outs:
+        assert np.array_equal(o.host(), y) and o.guards_intact()
+
+
+def test_write_bcast_440x5120_p8_workload():
+    w = W.WRITE_BCAST_440x5120
+    xs = I.make_inputs(w.dist, w.P, w.n, seed=0)
+    outs = [Guarded(w.n) for _ in range(w.P)]
+    announce(w.name)
+    ar.ar_oneshot_write_bcast([to_dev(x) for x in xs], [o.view for o in outs])
+    torch.cuda.synchronize()
+    y = O.oneshot_sum(xs)
+    for o in outs:
+        assert np.array_equal(o.host(), y)
+        assert o.guards_intact()
+
+
+# ------------------------------------------------------------------ two-shot
+
+@pytest.mark.parametrize("P,n", [(8, 1023), (8, 1024), (8, 1025), (8, 5000), (2, 300), (3, 1000),
+                                 (4, 4096 * 3 + 17), (8, 128 * 8 * 7 - 1)])
+def test_twoshot_every_owner_and_untouched_outside(P, n):
+    xs = _inputs(P, n, seed=P + n)
+    d_in = [to_dev(x) for x in xs]
+    outs = [Guarded(n, init=np.full(n, 0xA5A5, np.uint16)) for _ in range(P)]
+    prior = [np.full(n, 0xA5A5, np.uint16) for _ in range(P)]
+    for r in range(P):
+        announce(f"twoshot P={P} n={n} rank={r}")
+        ar.ar_twoshot_share(d_in, [o.view for o in outs], r)
+        torch.cuda.synchronize()
+        prior = O.twoshot_share(xs, r, prior)
+        for o, want in zip(outs, prior):
+            assert np.array_equal(o.host(), want), (r,)
+            assert o.guards_intact()
+
+
+def test_twoshot_680x5120_p8_rank3_workload():
+    w = W.TWOSHOT_680x5120_R3
+    xs = I.make_inputs(w.dist, w.P, w.n, seed=0)
+    fill = np.full(w.n, 0xA5A5, np.uint16)
+    outs = [Guarded(w.n, init=fill) for _ in range(w.P)]
+    announce(w.name)
+    ar.ar_twoshot_share([to_dev(x) for x in xs], [o.view for o in outs], 3)
+    torch.cuda.synchronize()
+    want = O.twoshot_share(xs, 3, [fill] * w.P)
+    b, e = O.slice_range(w.P, w.n, 3)
+    assert (b, e) == (1305600, 1740800)
+    for o, wt in zip(outs, want):
+        h = o.host()
+        assert np.array_equal(h, wt)
+        assert (h[:b] == 0xA5A5).all() and (h[e:] == 0xA5A5).all()
+        assert o.guards_intact()
+
+
+def test_twoshot_64Mi_p4_all_owners_workload():
+    w = W.TWOSHOT_64Mi_P4
+    announce(w.name + " (generating inputs)")
+    xs = I.make_inputs(w.dist, w.P, w.n, seed=0)
+    d_in = [to_dev(x) for x in xs]
+    d_out = [torch.full((w.n,), 0x2525, dtype=torch.int16, device="cuda:0") for _ in range(w.P)]
+    announce(w.name + " (owners 0..3)")
+    for r in w.ranks:
+        ar.ar_twoshot_share(d_in, d_out, r)
+    torch.cuda.synchronize()
+    announce(w.name + " (oracle)")
+    y = O.oneshot_sum(xs)
+    for t in d_out:
+        assert np.array_equal(to_host(t), y)
