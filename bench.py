@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Benchmark of the bf16 allreduce share on one MI355X.
+
+The headline workload is the write-mode one-shot share, P = 8 peers of
+440x5120 bf16 (2,252,800 elements each), the reduced result broadcast-written
+into 8 outputs.  A step is one ar_oneshot_write_bcast call on inputs already
+resident in HBM.  `value` is algorithmic bytes moved per second over the
+K timed steps (launched back to back on one stream, HIP events around the
+whole timed region).
+
+The same line also carries every other workload of the library (`rows`):
+one-shot 4096 x 8, the fused LL-packet share 512x7168 x 8 (graded launch of
+all eight ranks, flags rotating call to call), the two-shot share of rank 3
+at 680x5120 x 8, and the 4-owner two-shot at 64 Mi elements x 4.  Each row
+reports the streamed time per call (N back-to-back calls / N), the per-call
+time with an event pair around each call, and the per-call time after a
+512 MiB scrub evicts L2 and the 256 MB MALL ("cold"), each as algorithmic
+GB/s and a fraction of the 8 TB/s HBM peak.
+
+`roofline` is for the headline kernel: algorithmic bytes per launch over the
+mean launch duration measured with an event pair around each launch;
+`traffic` is the FETCH_SIZE + WRITE_SIZE bytes per launch recorded by
+rocprofv3 in profiles/, scaled by the same counters' reading for a plain copy
+of known size, or null when the kernels changed after the counters were
+taken.  `cpu_baseline` times the CPU oracle (test infrastructure) on the full
+headline workload, single-threaded.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --only-headline      (profiling runs: headline only)
+       python bench.py --copy-probe         (counter calibration: a plain copy)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import pathlib
+import re
+import sys
+import time
+
+ROOT = pathlib.Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+METRIC = "µs/call and effective HBM GB/s (% of MI355X peak), P=8 bf16 one-rank share"
+HBM_PEAK_GBS = 8000.0
+PROFILES = ROOT / "profiles"
+KERNEL_SOURCES = ["allreduce_reduction_way_amd/csrc/device.h",
+                  "allreduce_reduction_way_amd/csrc/host.h",
+                  "allreduce_reduction_way_amd/csrc/host.hip",
+                  "allreduce_reduction_way_amd/csrc/reduce.hip",
+                  "allreduce_reduction_way_amd/csrc/packet.hip"]
+COPY_PROBE_BYTES = 256 << 20
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        h.update((ROOT / rel).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------- setup
+
+class Row:
+    """One workload: device buffers plus a `step(i)` that launches one step."""
+
+    def __init__(self, name, alg_bytes, launches_per_step, step, note):
+        self.name, self.alg_bytes, self.launches = name, alg_bytes, launches_per_step
+        self.step, self.note = step, note
+
+
+def make_rows(names, torch, ar, I, W, stream):
+    dev = torch.device("cuda:0")
+
+    def dev_inputs(w, seed=0):
+        import numpy as np
+        return [torch.from_numpy(x.view(np.int16)).to(dev) for x in I.make_inputs(w.dist, w.P, w.n, seed)]
+
+    rows = {}
+    if W.WRITE_BCAST_440x5120.name in names:
+        w = W.WRITE_BCAST_440x5120
+        ins = dev_inputs(w)
+        outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
+        rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, 1,
+                           lambda i, ins=ins, outs=outs: ar.ar_oneshot_write_bcast(ins, outs, stream=stream),
+                           "read P inputs + write P outputs")
+    if W.ONESHOT_4K.name in names:
+        w = W.ONESHOT_4K
+        ins = dev_inputs(w)
+        out = torch.empty(w.n, dtype=torch.int16, device=dev)
+        rows[w.name] = Row(w.name, (w.P + 1) * w.n * 2, 1,
+                           lambda i, ins=ins, out=out: ar.ar_oneshot_sum(ins, out, stream=stream),
+                           "latency-bound: compare with the empty-kernel floor")
+    if W.PACKET_512x7168.name in names:
+        w = W.PACKET_512x7168
+        ins = dev_inputs(w)
+        nb = ar.ar_packet_scratch_bytes(w.P, w.n)
+        scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
+        outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
+        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        state = {"flag": 0}
+
+        def packet_step(i, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl, state=state):
+            state["flag"] += 1  # every call carries the next flag
+            ar.ar_packet_fused(ins, scratch, outs, state["flag"], ctrl, stream=stream)
+
+        row = Row(w.name, 20 * w.n * w.P, 1, packet_step,
+                  "graded launch: all 8 ranks; per rank 10n B read + 10n B written")
+        row.ctrl = ctrl
+        rows[w.name] = row
+    if W.TWOSHOT_680x5120_R3.name in names:
+        w = W.TWOSHOT_680x5120_R3
+        ins = dev_inputs(w)
+        outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
+        b, e = ar.ar_slice_range(w.P, 3, w.n)
+        rows[w.name] = Row(w.name, 2 * w.P * (e - b) * 2, 1,
+                           lambda i, ins=ins, outs=outs: ar.ar_twoshot_share(ins, outs, 3, stream=stream),
+                           "rank 3's slice: read P x slice, write P x slice")
+    if W.TWOSHOT_64Mi_P4.name in names:
+        w = W.TWOSHOT_64Mi_P4
+        ins = dev_inputs(w)
+        outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
+
+        def owners(i, ins=ins, outs=outs, w=w):
+            for r in w.ranks:
+                ar.ar_twoshot_share(ins, outs, r, stream=stream)
+
+        rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, len(w.ranks), owners,
+                           "4 owner launches per step, full buffer into 4 outputs")
+    return rows
+
+
+# ----------------------------------------------------------------------- timing
+
+def time_streamed(torch, stream, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def time_per_call(torch, stream, fn, calls, scrub=None):
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(calls)]
+    for i, (a, b) in enumerate(evs):
+        if scrub is not None:
+            with torch.cuda.stream(stream):
+                scrub.fill_(i & 0x7F)
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return {"mean_us": 1e3 * sum(ms) / len(ms), "median_us": 1e3 * ms[len(ms) // 2],
+            "best_us": 1e3 * ms[0], "worst_us": 1e3 * ms[-1]}
+
+
+def gbs(nbytes, us):
+    return nbytes / (us * 1e-6) / 1e9
+
+
+def traffic_from_profiles(headline: str, launches_alg_bytes: int):
+    """FETCH_SIZE + WRITE_SIZE per launch from the committed counter summary,
+    scaled by the copy-probe factor; None if absent or taken on other sources."""
+    path = PROFILES / f"{headline}_counters.md"
+    if not path.exists():
+        return None
+    text = path.read_text()
+    m = re.search(r"kernel source hash:\s*`?([0-9a-f]{16})", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    m = re.search(r"scaled HBM bytes per launch:\s*([0-9.]+)", text)
+    return float(m.group(1)) if m else None
+
+
+# -------------------------------------------------------------------- CPU leg
+
+def cpu_baseline(xs_host, budget_s=12.0):
+    """The oracle as it stands, single-threaded, on the full headline workload."""
+    from oracle import oracle as O
+    alg = 2 * len(xs_host) * xs_host[0].size * 2
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        O.write_bcast(xs_host)
+        calls += 1
+        el = time.perf_counter() - t0
+        if (el >= budget_s and calls >= 3) or calls >= 1000:
+            break
+    return {"value": round(alg * calls / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"full 440x5120 x 8 write-mode share, {calls} calls in {el:.1f} s "
+                      f"({1e3 * el / calls:.1f} ms/call), single thread"}
+
+
+# ------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--only-headline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cold-calls", type=int, default=20)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one rank's share on ONE GPU: every peer buffer is emulated in "
+              "this GPU's HBM and nothing crosses to a second GPU. Run it with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from allreduce_reduction_way_amd import ar, inputs as I, workloads as W
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU (torch.cuda.is_available() is False)")
+    ar.lib()
+    stream = torch.cuda.Stream()
+
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.int16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.steps} copies of {COPY_PROBE_BYTES} bytes")
+        return
+
+    headline = W.WRITE_BCAST_440x5120
+    names = [headline.name] if args.only_headline else [w.name for w in W.ALL]
+    log("allocating and filling inputs")
+    rows = make_rows(names, torch, ar, I, W, int(stream.cuda_stream))
+
+    # headline: streamed timed region
+    h = rows[headline.name]
+    log(f"headline {h.name}: {args.warmup} warm-up + {args.steps} timed steps")
+    ms, wall = time_streamed(torch, stream, h.step, args.steps, args.warmup)
+    per_call = time_per_call(torch, stream, h.step, max(50, min(args.steps, 500)))
+    achieved = gbs(h.alg_bytes, per_call["mean_us"])
+    traffic = traffic_from_profiles(headline.name, h.alg_bytes)
+    value = gbs(h.alg_bytes, ms * 1e3)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "us_per_call": round(ms * 1e3, 3),
+        "hbm_peak_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": headline.name, "P": headline.P, "n": headline.n,
+                   "elements": "bf16", "accumulate": "f32 in rank order, RNE to bf16",
+                   "alg_bytes_per_step": h.alg_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_reduce<8, true, U> (write mode, P = 8)",
+                     "mean_launch_us": round(per_call["mean_us"], 3)},
+        "wall_s_timed_region": round(wall, 4),
+    }
+
+    if not args.only_headline:
+        out_rows = {}
+        for name, row in rows.items():
+            log(f"row {name}")
+            steps = max(20, min(args.steps, 2000 if row.alg_bytes < (64 << 20) else 200))
+            ms_r, _ = time_streamed(torch, stream, row.step, steps, 10)
+            pc = time_per_call(torch, stream, row.step, 50)
+            scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+            cold = time_per_call(torch, stream, row.step, args.cold_calls, scrub=scrub)
+            del scrub
+            us = ms_r * 1e3
+            out_rows[name] = {
+                "streamed_us_per_call": round(us, 3),
+                "streamed_gbs": round(gbs(row.alg_bytes, us), 1),
+                "per_call_us": {k: round(v, 3) for k, v in pc.items()},
+                "per_call_gbs": round(gbs(row.alg_bytes, pc["mean_us"]), 1),
+                "cold_us": {k: round(v, 3) for k, v in cold.items()},
+                "cold_gbs": round(gbs(row.alg_bytes, cold["median_us"]), 1),
+                "frac_of_hbm_peak_streamed": round(gbs(row.alg_bytes, us) / HBM_PEAK_GBS, 4),
+                "frac_of_hbm_peak_cold": round(gbs(row.alg_bytes, cold["median_us"]) / HBM_PEAK_GBS, 4),
+                "alg_bytes_per_step": row.alg_bytes,
+                "launches_per_step": row.launches,
+                "note": row.note,
+            }
+            if hasattr(row, "ctrl"):
+                torch.cuda.synchronize()
+                out_rows[name]["device_status"] = int(row.ctrl.view(torch.int32)[0].item())
+        log("empty-kernel floor")
+        floor_ms, _ = time_streamed(torch, stream, lambda i: ar.ar_noop(stream=int(stream.cuda_stream)),
+                                    2000, 50)
+        floor_pc = time_per_call(torch, stream, lambda i: ar.ar_noop(stream=int(stream.cuda_stream)), 200)
+        out_rows["empty_kernel_floor"] = {"streamed_us_per_call": round(floor_ms * 1e3, 3),
+                                          "per_call_us": {k: round(v, 3) for k, v in floor_pc.items()}}
+        result["rows"] = out_rows
+
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        xs = I.make_inputs(headline.dist, headline.P, headline.n, seed=0)
+        cb = cpu_baseline(xs)
+        # the oracle's output for the sample, compared with the GPU's (side check)
+        from oracle import oracle as O
+        d_out = [torch.empty(headline.n, dtype=torch.int16, device="cuda:0") for _ in range(headline.P)]
+        ar.ar_oneshot_write_bcast([torch.from_numpy(x.view(np.int16)).cuda() for x in xs], d_out)
+        torch.cuda.synchronize()
+        y = O.oneshot_sum(xs)
+        cb["gpu_output_matches"] = all(np.array_equal(t.cpu().numpy().view(np.uint16), y) for t in d_out)
+        result["cpu_baseline"] = cb
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
