@@ -62,7 +62,7 @@ def lib() -> ctypes.CDLL:
             "ar_packet_scratch_bytes": (i64, [i32, i64]),
             "ar_strerror": (ctypes.c_char_p, [i32]),
             "ar_noop": (i32, [vp]),
-            "ar_set_reduce_tuning": (i32, [i32, i32]),
+            "ar_set_reduce_tuning": (i32, [i32, i32, i32]),
             "ar_set_packet_tuning": (i32, [i32]),
         }
         for name, (res, args) in sig.items():
@@ -190,8 +190,8 @@ def ar_noop(stream=None) -> None:
     _check(lib().ar_noop(_stream(stream)), "ar_noop")
 
 
-def ar_set_reduce_tuning(unroll: int = 0, max_blocks: int = 0) -> None:
-    _check(lib().ar_set_reduce_tuning(unroll, max_blocks), "ar_set_reduce_tuning")
+def ar_set_reduce_tuning(unroll: int = 0, threads: int = 0, max_blocks: int = 0) -> None:
+    _check(lib().ar_set_reduce_tuning(unroll, threads, max_blocks), "ar_set_reduce_tuning")
 
 
 def ar_set_packet_tuning(per_rank: int = 0) -> None:

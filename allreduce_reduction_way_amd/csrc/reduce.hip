@@ -35,8 +35,8 @@ struct ReduceArgs {
 template <int P, bool BCAST, int U>
 __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
     constexpr int NOUT = BCAST ? P : 1;
-    const int64_t nthreads = (int64_t)gridDim.x * kThreads;
-    const int64_t tid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
 
     for (int64_t v0 = tid; v0 < a.nvec; v0 += nthreads * U) {
         u32x4 x[U][P];
@@ -100,6 +100,7 @@ ReduceKernel pick(int P, int U) {
 
 // Launch shape overrides for benchmark sweeps (0 = automatic).
 int g_unroll_override = 0;
+int g_threads_override = 0;
 int g_max_blocks_override = 0;
 
 // Splits the range into scalar head, 16-byte bulk and scalar tail.  The bulk
@@ -143,16 +144,17 @@ int launch_reduce(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast
     int U = a.nvec <= (int64_t)dev.cus * kThreads ? 1 : 2;
     if (g_unroll_override == 1 || g_unroll_override == 2 || g_unroll_override == 4)
         U = g_unroll_override;
-    const int64_t per_block = (int64_t)kThreads * U;
+    const int threads = g_threads_override > 0 ? g_threads_override : kThreads;
+    const int64_t per_block = (int64_t)threads * U;
     int64_t blocks = (a.nvec + per_block - 1) / per_block;
-    const int64_t scalar_blocks = (a.head + a.ntail + kThreads - 1) / kThreads;
+    const int64_t scalar_blocks = (a.head + a.ntail + threads - 1) / threads;
     if (scalar_blocks > blocks) blocks = scalar_blocks;
     int64_t cap = (int64_t)dev.cus * 16;  // beyond this, lanes loop (grid stride)
     if (g_max_blocks_override > 0) cap = g_max_blocks_override;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
     ReduceKernel fn = bcast ? pick<true>(P, U) : pick<false>(P, U);
-    return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, kThreads, a, stream);
+    return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, (unsigned)threads, a, stream);
 }
 
 ar_ptrs offset_ptrs(const ar_ptrs &p, int count, int64_t elem) {
@@ -220,10 +222,12 @@ int ar_twoshot_share(ar_ptrs in, ar_ptrs out, int P, int rank, int64_t n, void *
 }
 
 // Benchmark-only launch-shape override for the three entry points above.
-int ar_set_reduce_tuning(int unroll, int max_blocks) {
-    if (!(unroll == 0 || unroll == 1 || unroll == 2 || unroll == 4) || max_blocks < 0)
+int ar_set_reduce_tuning(int unroll, int threads, int max_blocks) {
+    if (!(unroll == 0 || unroll == 1 || unroll == 2 || unroll == 4) || max_blocks < 0 ||
+        !(threads == 0 || threads == 64 || threads == 128 || threads == 256))
         return AR_EINVAL;
     g_unroll_override = unroll;
+    g_threads_override = threads;
     g_max_blocks_override = max_blocks;
     return AR_OK;
 }
