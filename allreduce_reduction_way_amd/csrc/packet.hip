@@ -7,35 +7,34 @@
 // arrival from the data itself (ARK PR #254 "Add monolithic fused packet
 // allreduce kernel and Model::all_reduce_packet API", description).
 //
-// Work is laid out word-per-lane: lane t of a 256-lane workgroup handles
-// words t and t + 256 of a 512-word chunk, so every 64-lane wavefront issues
-// one 512-byte contiguous atomic access per instruction and one 256-byte
-// contiguous element access.
+// Work is laid out word-per-lane: lane t of a 256-lane workgroup handles word
+// t (and t + 256 when a chunk is two words per lane) of each slot's chunk, so
+// every 64-lane wavefront issues 512-byte contiguous atomic accesses and
+// 256-byte contiguous element accesses.
 //
 // The fused kernel runs the P emulated ranks as groups of workgroups of one
-// persistent grid: workgroup b serves rank lo + b % R and chunks b / R,
-// b / R + B, ... (R ranks in the launch, B workgroups per rank).  Rank r on
-// chunk c does, for each of its words:
+// persistent grid: workgroup b serves rank lo + b % R and chunks m, m + B,
+// m + 2B, ... with m = b / R (R ranks in the launch, B workgroups per rank).
+// Rank r on chunk c does, for each of its words:
 //   scatter    x_r[slice j] -> inbox_j[slot r]           for j = 0..P-1
 //   reduce     inbox_r[slot 0..P-1] -> rank-order sum     (waits on flags)
 //   broadcast  sum -> resbox_j[slot r]                    for j = 0..P-1
 //   receive    resbox_r[slot 0..P-1] -> out_r             (waits on flags)
+// and the three stages of consecutive chunks overlap in a software pipeline.
 // The only synchronisation between workgroups is the flag inside each word:
 // lane t of rank r waits only on lane t of the other ranks' workgroups of the
-// same chunk, and every lane writes all it produces before it waits
-// (torchcomms PR #3850 "Add HIP-graph capture coverage for the sharded-relay
-// collectives", commit summary D117629704: pairwise handshakes, no global
-// barrier, write and flag before waiting).  The grid never exceeds the number
-// of workgroups that fit on the device at once, so every workgroup a lane
-// waits on is resident; all waits are bounded and report AR_ETIMEDOUT.
+// same m, and everything a lane waits on was written before its producer
+// could wait on anything later (torchcomms PR #3850 "Add HIP-graph capture
+// coverage for the sharded-relay collectives", commit summary D117629704:
+// pairwise handshakes, no global barrier, write and flag before waiting).
+// The grid never exceeds the number of workgroups that fit on the device at
+// once, so every workgroup a lane waits on is resident; all waits are bounded
+// and report AR_ETIMEDOUT.
 #include "device.h"
 #include "host.h"
 
 namespace ar {
 namespace {
-
-constexpr int kWordsPerLane = 2;
-constexpr int64_t kChunkWords = (int64_t)kThreads * kWordsPerLane;  // 512 words = 1024 bf16
 
 // Two bf16 starting at element e of a slice of `len` elements (e even, e < len
 // or the word is padding), packed low element first; elements past the slice
@@ -101,7 +100,7 @@ struct FusedArgs {
     int64_t n;
     int64_t L;        // length of slices 0..P-2; the last one is n - (P-1) L
     int64_t slot_words;  // 2 x packets per slot
-    int64_t chunks;   // chunks of kChunkWords words covering a slot
+    int64_t chunks;   // chunks of chunk_words words covering a slot
     int rank_lo;
     int nranks;       // R
     int per_rank;     // B
@@ -111,116 +110,149 @@ struct FusedArgs {
     uint64_t max_spins;
 };
 
-template <int P>
+// Words of slice j's slot that carry data (2 per packet).
+__device__ __forceinline__ int64_t slice_len(const FusedArgs &a, int j, int P) {
+    return j == P - 1 ? a.n - (int64_t)(P - 1) * a.L : a.L;
+}
+
+// scatter: x_r[slice j] -> inbox_j[slot r], every j (all loads, then all stores)
+template <int P, int WPL>
+__device__ __forceinline__ void scatter(const FusedArgs &a, int r, int64_t c) {
+    const uint16_t *x_r = static_cast<const uint16_t *>(a.in.p[r]);
+    const int64_t w0 = c * (kThreads * WPL) + threadIdx.x;
+    uint32_t d[P][WPL];
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const int64_t len = slice_len(a, j, P);
+#pragma unroll
+        for (int k = 0; k < WPL; ++k)
+            d[j][k] = load_pair(x_r + j * a.L, 2 * (w0 + k * kThreads), len, a.aligned4);
+    }
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+        const int64_t words = 2 * ((slice_len(a, j, P) + 3) / 4);
+        uint64_t *slot = static_cast<uint64_t *>(a.scratch.p[j]) + (int64_t)r * a.slot_words;
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            const int64_t w = w0 + k * kThreads;
+            if (w < words) store_word(slot + w, make_word(d[j][k], a.flag));
+        }
+    }
+}
+
+// reduce + broadcast: inbox_r[slot 0..P-1] -> rank-order sum -> resbox_j[slot r]
+template <int P, int WPL>
+__device__ __forceinline__ bool reduce_broadcast(const FusedArgs &a, int r, int64_t c) {
+    const uint64_t *mine = static_cast<const uint64_t *>(a.scratch.p[r]);
+    const int64_t words = 2 * ((slice_len(a, r, P) + 3) / 4);
+    const int64_t w0 = c * (kThreads * WPL) + threadIdx.x;
+    uint64_t v[WPL][P];
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) {
+        const int64_t w = w0 + k * kThreads;
+#pragma unroll
+        for (int s = 0; s < P; ++s)
+            v[k][s] = w < words ? load_word(mine + (int64_t)s * a.slot_words + w) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < WPL; ++k) {
+        const int64_t w = w0 + k * kThreads;
+        if (w >= words) continue;
+        uint32_t dw[P];
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            if (word_flag(v[k][s]) != a.flag &&
+                !wait_word(mine + (int64_t)s * a.slot_words + w, a.flag, v[k][s], a.status,
+                           a.max_spins))
+                return false;
+            dw[s] = word_data(v[k][s]);
+        }
+        const uint64_t res = make_word(reduce_word<P>(dw), a.flag);
+#pragma unroll
+        for (int j = 0; j < P; ++j)
+            store_word(static_cast<uint64_t *>(a.scratch.p[j]) + (int64_t)(P + r) * a.slot_words + w,
+                       res);
+    }
+    return true;
+}
+
+// receive: resbox_r[slot s] (the reduced slice s) -> out_r[slice s]
+template <int P, int WPL>
+__device__ __forceinline__ bool receive(const FusedArgs &a, int r, int64_t c) {
+    const uint64_t *mine = static_cast<const uint64_t *>(a.scratch.p[r]);
+    uint16_t *out_r = static_cast<uint16_t *>(a.out.p[r]);
+    const int64_t w0 = c * (kThreads * WPL) + threadIdx.x;
+    uint64_t v[P][WPL];
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+        const int64_t len = slice_len(a, s, P);
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            const int64_t w = w0 + k * kThreads;
+            v[s][k] = 2 * w < len ? load_word(mine + (int64_t)(P + s) * a.slot_words + w)
+                                  : make_word(0, a.flag);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < P; ++s) {
+        const int64_t len = slice_len(a, s, P);
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            const int64_t w = w0 + k * kThreads;
+            if (2 * w >= len) continue;
+            if (word_flag(v[s][k]) != a.flag &&
+                !wait_word(mine + (int64_t)(P + s) * a.slot_words + w, a.flag, v[s][k], a.status,
+                           a.max_spins))
+                return false;
+            store_pair(out_r + s * a.L, 2 * w, len, a.aligned4, word_data(v[s][k]));
+        }
+    }
+    return true;
+}
+
+// Workgroup b serves rank lo + b % R and its chunks m, m + B, m + 2B, ...
+// (m = b / R) as a three-stage software pipeline: step i scatters chunk i,
+// reduces and broadcasts chunk i-1 and receives chunk i-2.  Everything a
+// step waits on was produced by the other ranks' workgroups of the same m in
+// their step i-1, before they could wait on anything in step i, so by
+// induction over steps every wait is satisfied, and a wait normally finds its
+// packets already there.
+template <int P, int WPL>
 __global__ __launch_bounds__(kThreads) void k_packet_fused(FusedArgs a) {
     const int r = a.rank_lo + (int)(blockIdx.x % (unsigned)a.nranks);
-    const int64_t first_chunk = blockIdx.x / (unsigned)a.nranks;
-    const uint16_t *x_r = static_cast<const uint16_t *>(a.in.p[r]);
-    uint16_t *out_r = static_cast<uint16_t *>(a.out.p[r]);
-    uint64_t *mine = static_cast<uint64_t *>(a.scratch.p[r]);
-    const int64_t last_len = a.n - (int64_t)(P - 1) * a.L;
-
-    for (int64_t c = first_chunk; c < a.chunks; c += a.per_rank) {
-        const int64_t w0 = c * kChunkWords + threadIdx.x;
-
-        // scatter: every load first, then every store
-        uint32_t d[P][kWordsPerLane];
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const int64_t len = j == P - 1 ? last_len : a.L;
-#pragma unroll
-            for (int k = 0; k < kWordsPerLane; ++k) {
-                const int64_t w = w0 + k * kThreads;
-                d[j][k] = load_pair(x_r + j * a.L, 2 * w, len, a.aligned4);
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const int64_t len = j == P - 1 ? last_len : a.L;
-            const int64_t words = 2 * ((len + 3) / 4);
-            uint64_t *slot = static_cast<uint64_t *>(a.scratch.p[j]) + (int64_t)r * a.slot_words;
-#pragma unroll
-            for (int k = 0; k < kWordsPerLane; ++k) {
-                const int64_t w = w0 + k * kThreads;
-                if (w < words) store_word(slot + w, make_word(d[j][k], a.flag));
-            }
-        }
-
-        // reduce + broadcast of slice r
-        {
-            const int64_t len = r == P - 1 ? last_len : a.L;
-            const int64_t words = 2 * ((len + 3) / 4);
-#pragma unroll
-            for (int k = 0; k < kWordsPerLane; ++k) {
-                const int64_t w = w0 + k * kThreads;
-                if (w >= words) continue;
-                uint64_t v[P];
-#pragma unroll
-                for (int s = 0; s < P; ++s) v[s] = load_word(mine + (int64_t)s * a.slot_words + w);
-                uint32_t dw[P];
-#pragma unroll
-                for (int s = 0; s < P; ++s) {
-                    if (word_flag(v[s]) != a.flag &&
-                        !wait_word(mine + (int64_t)s * a.slot_words + w, a.flag, v[s], a.status,
-                                   a.max_spins))
-                        return;
-                    dw[s] = word_data(v[s]);
-                }
-                const uint64_t res = make_word(reduce_word<P>(dw), a.flag);
-#pragma unroll
-                for (int j = 0; j < P; ++j)
-                    store_word(static_cast<uint64_t *>(a.scratch.p[j]) +
-                                   (int64_t)(P + r) * a.slot_words + w,
-                               res);
-            }
-        }
-
-        // receive: resbox_r[slot s] holds the reduced slice s
-        uint64_t v[P][kWordsPerLane];
-#pragma unroll
-        for (int s = 0; s < P; ++s) {
-            const int64_t len = s == P - 1 ? last_len : a.L;
-            const int64_t words = 2 * ((len + 3) / 4);
-#pragma unroll
-            for (int k = 0; k < kWordsPerLane; ++k) {
-                const int64_t w = w0 + k * kThreads;
-                v[s][k] = w < words ? load_word(mine + (int64_t)(P + s) * a.slot_words + w)
-                                    : make_word(0, a.flag);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < P; ++s) {
-            const int64_t len = s == P - 1 ? last_len : a.L;
-#pragma unroll
-            for (int k = 0; k < kWordsPerLane; ++k) {
-                const int64_t w = w0 + k * kThreads;
-                if (2 * w >= len) continue;
-                if (word_flag(v[s][k]) != a.flag &&
-                    !wait_word(mine + (int64_t)(P + s) * a.slot_words + w, a.flag, v[s][k],
-                               a.status, a.max_spins))
-                    return;
-                store_pair(out_r + s * a.L, 2 * w, len, a.aligned4, word_data(v[s][k]));
-            }
-        }
+    const int64_t m = blockIdx.x / (unsigned)a.nranks;
+    const int64_t B = a.per_rank;
+    const int64_t mine = m < a.chunks ? (a.chunks - 1 - m) / B + 1 : 0;
+    for (int64_t i = 0; i < mine + 2; ++i) {
+        if (i < mine) scatter<P, WPL>(a, r, m + i * B);
+        if (i >= 1 && i <= mine && !reduce_broadcast<P, WPL>(a, r, m + (i - 1) * B)) return;
+        if (i >= 2 && !receive<P, WPL>(a, r, m + (i - 2) * B)) return;
     }
 }
 
 typedef void (*FusedKernel)(FusedArgs);
 
-FusedKernel pick_fused(int P) {
+template <int WPL>
+FusedKernel pick_fused_wpl(int P) {
     switch (P) {
-        case 2: return k_packet_fused<2>;
-        case 3: return k_packet_fused<3>;
-        case 4: return k_packet_fused<4>;
-        case 5: return k_packet_fused<5>;
-        case 6: return k_packet_fused<6>;
-        case 7: return k_packet_fused<7>;
-        default: return k_packet_fused<8>;
+        case 2: return k_packet_fused<2, WPL>;
+        case 3: return k_packet_fused<3, WPL>;
+        case 4: return k_packet_fused<4, WPL>;
+        case 5: return k_packet_fused<5, WPL>;
+        case 6: return k_packet_fused<6, WPL>;
+        case 7: return k_packet_fused<7, WPL>;
+        default: return k_packet_fused<8, WPL>;
     }
 }
 
-// Launch-shape override for benchmark sweeps: workgroups per rank (0 = auto).
+FusedKernel pick_fused(int P, int wpl) {
+    return wpl == 2 ? pick_fused_wpl<2>(P) : pick_fused_wpl<1>(P);
+}
+
+// Launch-shape overrides for benchmark sweeps: workgroups per rank and words
+// per lane per chunk (0 = automatic).
 int g_fused_per_rank_override = 0;
+int g_fused_wpl_override = 0;
 
 }  // namespace
 }  // namespace ar
@@ -313,7 +345,8 @@ int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo
 
     DeviceInfo dev;
     if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
-    FusedKernel fn = pick_fused(P);
+    const int wpl = g_fused_wpl_override ? g_fused_wpl_override : 1;
+    FusedKernel fn = pick_fused(P, wpl);
     const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(fn));
     if (per_cu <= 0) return AR_ELAUNCH;
 
@@ -324,7 +357,8 @@ int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo
     a.n = n;
     a.L = slice_len_unit(P, n);
     a.slot_words = 2 * ar_packet_slot_packets(P, n);
-    a.chunks = (a.slot_words + kChunkWords - 1) / kChunkWords;
+    const int64_t chunk_words = (int64_t)kThreads * wpl;
+    a.chunks = (a.slot_words + chunk_words - 1) / chunk_words;
     a.rank_lo = rank_lo;
     a.nranks = rank_hi - rank_lo;
     a.flag = flag;
@@ -352,9 +386,11 @@ int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo
 
 // Benchmark-only override of the fused kernel's workgroups per rank (0 = auto;
 // never above the resident limit).
-int ar_set_packet_tuning(int per_rank) {
-    if (per_rank < 0) return AR_EINVAL;
+int ar_set_packet_tuning(int per_rank, int words_per_lane) {
+    if (per_rank < 0 || !(words_per_lane == 0 || words_per_lane == 1 || words_per_lane == 2))
+        return AR_EINVAL;
     g_fused_per_rank_override = per_rank;
+    g_fused_wpl_override = words_per_lane;
     return AR_OK;
 }
 

@@ -139,19 +139,37 @@ int launch_reduce(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast
     ReduceArgs a;
     split_range(in_at, out_at, P, bcast ? P : 1, len, &a);
 
-    // Unroll: a small bulk is latency-bound, so spread it one vector per lane;
-    // a large one wants several vectors in flight per lane.
-    int U = a.nvec <= (int64_t)dev.cus * kThreads ? 1 : 2;
-    if (g_unroll_override == 1 || g_unroll_override == 2 || g_unroll_override == 4)
+    // Launch shape (swept on MI355X over workgroup size, unroll and grid):
+    //  - a small bulk (<= 256 lanes' worth per CU) is latency-bound: one vector
+    //    per lane in 64-lane workgroups, so the work spreads over every CU;
+    //  - a larger one takes 256-lane workgroups with two vectors in flight
+    //    per lane and exactly two workgroups per CU, looping (grid stride)
+    //    beyond that: a grid that is a multiple of the CU count keeps the
+    //    CUs evenly loaded (550 workgroups on 256 CUs ran 19% slower than 512).
+    int threads, U;
+    int64_t blocks;
+    if (a.nvec <= (int64_t)dev.cus * kThreads) {
+        threads = 64;
+        U = 1;
+        blocks = (a.nvec + threads - 1) / threads;
+    } else {
+        threads = kThreads;
+        U = 2;
+        blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
+        if (blocks > 2 * (int64_t)dev.cus) blocks = 2 * (int64_t)dev.cus;
+    }
+    if (g_unroll_override == 1 || g_unroll_override == 2 || g_unroll_override == 4) {
         U = g_unroll_override;
-    const int threads = g_threads_override > 0 ? g_threads_override : kThreads;
-    const int64_t per_block = (int64_t)threads * U;
-    int64_t blocks = (a.nvec + per_block - 1) / per_block;
+        blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
+    }
+    if (g_threads_override > 0) {
+        threads = g_threads_override;
+        blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
+    }
+    if (g_max_blocks_override > 0 && blocks > g_max_blocks_override) blocks = g_max_blocks_override;
     const int64_t scalar_blocks = (a.head + a.ntail + threads - 1) / threads;
     if (scalar_blocks > blocks) blocks = scalar_blocks;
-    int64_t cap = (int64_t)dev.cus * 16;  // beyond this, lanes loop (grid stride)
-    if (g_max_blocks_override > 0) cap = g_max_blocks_override;
-    if (blocks > cap) blocks = cap;
+    if (blocks > (int64_t)dev.cus * 16) blocks = (int64_t)dev.cus * 16;  // lanes loop beyond
     if (blocks < 1) blocks = 1;
     ReduceKernel fn = bcast ? pick<true>(P, U) : pick<false>(P, U);
     return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, (unsigned)threads, a, stream);

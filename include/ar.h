@@ -203,11 +203,12 @@ int ar_noop(void *stream);
  * ar_set_reduce_tuning: unroll (vectors in flight per lane) in {0 = automatic,
  * 1, 2, 4}, workgroup size in {0 = automatic, 64, 128, 256} and a cap on
  * workgroups (0 = automatic) for ar_oneshot_sum, ar_oneshot_write_bcast and
- * ar_twoshot_share.  ar_set_packet_tuning:
- * workgroups per emulated rank of ar_packet_fused (0 = automatic; never more
- * than fit on the device at once).  Results do not depend on either. */
+ * ar_twoshot_share.  ar_set_packet_tuning: workgroups per emulated rank of
+ * ar_packet_fused (0 = automatic; never more than fit on the device at once)
+ * and words per lane per chunk in {0 = automatic, 1, 2}.  Results do not
+ * depend on either. */
 int ar_set_reduce_tuning(int unroll, int threads, int max_blocks);
-int ar_set_packet_tuning(int per_rank);
+int ar_set_packet_tuning(int per_rank, int words_per_lane);
 
 #ifdef __cplusplus
 }

@@ -218,7 +218,7 @@ def test_packet_split_launch_with_skewed_producers():
     ctrl_a, ctrl_b = ctrl_block(), ctrl_block()
     s_a, s_b = torch.cuda.Stream(), torch.cuda.Stream()
     torch.cuda.synchronize()
-    ar.ar_set_packet_tuning(8)       # small grids, so both launches are resident together
+    ar.ar_set_packet_tuning(8, 0)       # small grids, so both launches are resident together
     try:
         announce("packet split launch: ranks 0..3 now, ranks 4..7 after 50 ms")
         ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl_a, rank_lo=0, rank_hi=4, stream=s_a)
@@ -226,8 +226,36 @@ def test_packet_split_launch_with_skewed_producers():
         ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl_b, rank_lo=4, rank_hi=8, stream=s_b)
         torch.cuda.synchronize()
     finally:
-        ar.ar_set_packet_tuning(0)
+        ar.ar_set_packet_tuning(0, 0)
     assert ctrl_status(ctrl_a) == 0 and ctrl_status(ctrl_b) == 0
     y = O.oneshot_sum(xs)
     for t in outs:
         assert np.array_equal(to_host(t), y)
+
+
+@pytest.mark.parametrize("per_rank,wpl", [(1, 1), (3, 2), (7, 1), (0, 1), (0, 2), (64, 2)])
+@pytest.mark.parametrize("P,n", [(8, 8192 * 9 + 1), (3, 4096 * 7 + 5)])
+def test_packet_fused_every_launch_shape(per_rank, wpl, P, n):
+    """Pipeline depth (chunks per workgroup) and chunk width change the
+    schedule, never the result: outputs and scratch images stay bit-exact."""
+    xs = I.make_inputs("uniform", P, n, seed=per_rank + wpl)
+    scratch = _scratch(P, n)
+    outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ctrl = ctrl_block()
+    ar.ar_set_packet_tuning(per_rank, wpl)
+    try:
+        announce(f"packet launch shape per_rank={per_rank} wpl={wpl} P={P} n={n}")
+        for f in (1, 2):
+            ar.ar_packet_fused([to_dev(x) for x in xs], scratch, outs, f, ctrl)
+        torch.cuda.synchronize()
+    finally:
+        ar.ar_set_packet_tuning(0, 0)
+    assert ctrl_status(ctrl) == 0
+    zero = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    _, img1 = O.packet_fused(xs, 1, zero)
+    want, img2 = O.packet_fused(xs, 2, img1)
+    for r in range(P):
+        assert np.array_equal(to_host(outs[r]), want[r])
+    got = _images(scratch)
+    for r in range(P):
+        assert np.array_equal(got[r], img2[r])
