@@ -57,6 +57,12 @@ def lib() -> ctypes.CDLL:
             "ar_ll_decode": (i32, [vp, vp, i64, u32, vp, u64, vp]),
             "ar_packet_fused": (i32, [ar_ptrs, ar_ptrs, ar_ptrs, i32, i32, i32, i64, u32, vp,
                                       u64, vp]),
+            "ar_reduce_scatter_share": (i32, [ar_ptrs, vp, i32, i32, i64, vp]),
+            "ar_packet_fused_epoch": (i32, [ar_ptrs, ar_ptrs, ar_ptrs, i32, i32, i32, i64, vp, u64,
+                                            vp]),
+            "ar_packet_send": (i32, [ar_ptrs, ar_ptrs, i32, i32, i32, i64, u32, vp]),
+            "ar_packet_recv_reduce_send": (i32, [ar_ptrs, i32, i32, i32, i64, u32, vp, u64, vp]),
+            "ar_packet_recv": (i32, [ar_ptrs, ar_ptrs, i32, i32, i32, i64, u32, vp, u64, vp]),
             "ar_slice_range": (i32, [i32, i32, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
             "ar_packet_slot_packets": (i64, [i32, i64]),
             "ar_packet_scratch_bytes": (i64, [i32, i64]),
@@ -162,6 +168,57 @@ def ar_packet_fused(inputs: Sequence, scratch: Sequence, outputs: Sequence, flag
     _check(lib().ar_packet_fused(_ptrs(inputs), _ptrs(scratch), _ptrs(outputs), P, rank_lo, hi,
                                  _n(n, inputs), flag, _addr(ctrl), max_spins, _stream(stream)),
            "ar_packet_fused")
+
+
+def ar_reduce_scatter_share(inputs: Sequence, out, rank: int, recvcount: int | None = None,
+                            stream=None) -> None:
+    P = len(inputs)
+    rc = _numel(out) if recvcount is None else int(recvcount)
+    _check(lib().ar_reduce_scatter_share(_ptrs(inputs), _addr(out), P, rank, rc, _stream(stream)),
+           "ar_reduce_scatter_share")
+
+
+def ar_packet_fused_epoch(inputs: Sequence, scratch: Sequence, outputs: Sequence, ctrl,
+                          rank_lo: int = 0, rank_hi: int | None = None, n: int | None = None,
+                          max_spins: int = 0, stream=None) -> None:
+    P = len(inputs)
+    if len(scratch) != P or len(outputs) != P:
+        raise ValueError("the packet path needs P inputs, P scratch buffers and P outputs")
+    hi = P if rank_hi is None else rank_hi
+    _check(lib().ar_packet_fused_epoch(_ptrs(inputs), _ptrs(scratch), _ptrs(outputs), P, rank_lo,
+                                       hi, _n(n, inputs), _addr(ctrl), max_spins, _stream(stream)),
+           "ar_packet_fused_epoch")
+
+
+def ar_packet_send(inputs: Sequence, scratch: Sequence, flag: int, rank_lo: int = 0,
+                   rank_hi: int | None = None, n: int | None = None, stream=None) -> None:
+    P = len(inputs)
+    if len(scratch) != P:
+        raise ValueError("need P scratch buffers")
+    hi = P if rank_hi is None else rank_hi
+    _check(lib().ar_packet_send(_ptrs(inputs), _ptrs(scratch), P, rank_lo, hi, _n(n, inputs),
+                                flag, _stream(stream)), "ar_packet_send")
+
+
+def ar_packet_recv_reduce_send(scratch: Sequence, n: int, flag: int, ctrl, rank_lo: int = 0,
+                               rank_hi: int | None = None, max_spins: int = 0,
+                               stream=None) -> None:
+    P = len(scratch)
+    hi = P if rank_hi is None else rank_hi
+    _check(lib().ar_packet_recv_reduce_send(_ptrs(scratch), P, rank_lo, hi, int(n), flag,
+                                            _addr(ctrl), max_spins, _stream(stream)),
+           "ar_packet_recv_reduce_send")
+
+
+def ar_packet_recv(scratch: Sequence, outputs: Sequence, flag: int, ctrl, rank_lo: int = 0,
+                   rank_hi: int | None = None, n: int | None = None, max_spins: int = 0,
+                   stream=None) -> None:
+    P = len(scratch)
+    if len(outputs) != P:
+        raise ValueError("need P outputs")
+    hi = P if rank_hi is None else rank_hi
+    _check(lib().ar_packet_recv(_ptrs(scratch), _ptrs(outputs), P, rank_lo, hi, _n(n, outputs),
+                                flag, _addr(ctrl), max_spins, _stream(stream)), "ar_packet_recv")
 
 
 def ar_slice_range(P: int, rank: int, n: int) -> tuple:

@@ -106,7 +106,9 @@ struct FusedArgs {
     int per_rank;     // B
     uint32_t flag;
     int aligned4;
-    int32_t *status;
+    int32_t *status;   // ar_ctrl.status (the control block's first word)
+    uint32_t *epoch;   // ar_ctrl.epoch (second word)
+    uint32_t *arrivals;  // ar_ctrl.arrivals (third word)
     uint64_t max_spins;
 };
 
@@ -232,8 +234,19 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, int r, bool do
 // their step i-1, before they could wait on anything in step i, so by
 // induction over steps every wait is satisfied, and a wait normally finds its
 // packets already there.
-template <int P, int WPL>
+//
+// EPOCH: the flag is not a kernel argument but ar_ctrl.epoch + 1, read by
+// every lane at the start; the last workgroup to finish stores it back as the
+// new epoch.  A launch captured in a graph then uses a new flag on every
+// replay instead of the one baked in at capture (torchcomms PR #3850, PR
+// summary, hazard G2: a by-value epoch replayed is already satisfied by every
+// flag).  Every workgroup reads the epoch before it counts itself in, and the
+// count completes only after the last one has, so all of them use one flag.
+template <int P, int WPL, bool EPOCH>
 __global__ __launch_bounds__(kThreads) void k_packet_fused(FusedArgs a) {
+    if (EPOCH) {
+        a.flag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    }
     const int r = a.rank_lo + (int)(blockIdx.x % (unsigned)a.nranks);
     const int64_t m = blockIdx.x / (unsigned)a.nranks;
     const int64_t B = a.per_rank;
@@ -241,33 +254,182 @@ __global__ __launch_bounds__(kThreads) void k_packet_fused(FusedArgs a) {
     for (int64_t i = 0; i < mine + 2; ++i) {
         if (!pipeline_step<P, WPL>(a, r, i < mine, m + i * B, i >= 1 && i <= mine,
                                    m + (i - 1) * B, i >= 2, m + (i - 2) * B))
-            return;
+            break;
+    }
+    if (EPOCH) {
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t before = __hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            if (before == gridDim.x - 1) {
+                __hip_atomic_store(a.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.epoch, a.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+    }
+}
+
+// The three-operation decomposition, one launch per phase (ARK PR #254,
+// description: the send_packet -> recv_reduce_send_packet -> recv_packet
+// pipeline that the fused kernel replaces): PHASE 0 scatters, 1 reduces and
+// broadcasts, 2 receives.  Each (rank, chunk) item is independent within a
+// launch; waits are on packets of the previous phase's launch (or of another
+// stream's).
+template <int P, int WPL, int PHASE>
+__global__ __launch_bounds__(kThreads) void k_packet_phase(FusedArgs a) {
+    const int64_t items = (int64_t)a.nranks * a.chunks;
+    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int r = a.rank_lo + (int)(it % a.nranks);
+        const int64_t c = it / a.nranks;
+        if (!pipeline_step<P, WPL>(a, r, PHASE == 0, c, PHASE == 1, c, PHASE == 2, c)) return;
     }
 }
 
 typedef void (*FusedKernel)(FusedArgs);
 
-template <int WPL>
-FusedKernel pick_fused_wpl(int P) {
-    switch (P) {
-        case 2: return k_packet_fused<2, WPL>;
-        case 3: return k_packet_fused<3, WPL>;
-        case 4: return k_packet_fused<4, WPL>;
-        case 5: return k_packet_fused<5, WPL>;
-        case 6: return k_packet_fused<6, WPL>;
-        case 7: return k_packet_fused<7, WPL>;
-        default: return k_packet_fused<8, WPL>;
+template <int P, int WPL>
+FusedKernel pick_kind(int kind) {
+    switch (kind) {
+        case 0: return k_packet_fused<P, WPL, false>;
+        case 1: return k_packet_fused<P, WPL, true>;
+        case 2: return k_packet_phase<P, WPL, 0>;
+        case 3: return k_packet_phase<P, WPL, 1>;
+        default: return k_packet_phase<P, WPL, 2>;
     }
 }
 
-FusedKernel pick_fused(int P, int wpl) {
-    return wpl == 2 ? pick_fused_wpl<2>(P) : pick_fused_wpl<1>(P);
+template <int WPL>
+FusedKernel pick_p(int P, int kind) {
+    switch (P) {
+        case 2: return pick_kind<2, WPL>(kind);
+        case 3: return pick_kind<3, WPL>(kind);
+        case 4: return pick_kind<4, WPL>(kind);
+        case 5: return pick_kind<5, WPL>(kind);
+        case 6: return pick_kind<6, WPL>(kind);
+        case 7: return pick_kind<7, WPL>(kind);
+        default: return pick_kind<8, WPL>(kind);
+    }
 }
+
+enum Kind { kFused = 0, kFusedEpoch = 1, kSend = 2, kRecvReduceSend = 3, kRecv = 4 };
 
 // Launch-shape overrides for benchmark sweeps: workgroups per rank and words
 // per lane per chunk (0 = automatic).
 int g_fused_per_rank_override = 0;
 int g_fused_wpl_override = 0;
+
+// Validates one packet-path call and fills the kernel arguments.  `use_in`,
+// `use_out`, `use_ctrl` say which buffers the entry point touches; every
+// table it uses needs P non-null pointers; no two distinct buffers it uses may
+// share a byte (identical input pointers are fine: inputs are only read).
+int prepare_packet(const ar_ptrs &in, const ar_ptrs &scratch, const ar_ptrs &out, bool use_in,
+                   bool use_out, bool use_ctrl, int P, int rank_lo, int rank_hi, int64_t n,
+                   uint32_t flag, bool need_flag, void *ctrl, uint64_t max_spins, int wpl,
+                   FusedArgs *a) {
+    if (!valid_P(P) || n < 0 || rank_lo < 0 || rank_hi > P || rank_lo >= rank_hi) return AR_EINVAL;
+    if (need_flag && flag == 0) return AR_EINVAL;
+    if (use_ctrl && (!ctrl || !aligned_to(ctrl, 4))) return AR_EINVAL;
+    for (int p = 0; p < P; ++p) {
+        if (!scratch.p[p] || !aligned_to(scratch.p[p], 16)) return AR_EINVAL;
+        if (use_in && (!in.p[p] || !aligned_to(in.p[p], 2))) return AR_EINVAL;
+        if (use_out && (!out.p[p] || !aligned_to(out.p[p], 2))) return AR_EINVAL;
+    }
+    if (n == 0) return AR_OK;
+    const int64_t sbytes = ar_packet_scratch_bytes(P, n);
+    Span spans[3 * AR_MAX_P + 1];
+    int kind[3 * AR_MAX_P + 1];
+    int ns = 0;
+    for (int p = 0; p < P; ++p) {
+        if (use_in) {
+            spans[ns] = span_of(in.p[p], 0, n, 2);
+            kind[ns++] = 0;
+        }
+        if (use_out) {
+            spans[ns] = span_of(out.p[p], 0, n, 2);
+            kind[ns++] = 1;
+        }
+        spans[ns] = span_of(scratch.p[p], 0, sbytes, 1);
+        kind[ns++] = 2;
+    }
+    if (use_ctrl) {
+        spans[ns] = span_of(ctrl, 0, AR_CTRL_BYTES, 1);
+        kind[ns++] = 3;
+    }
+    for (int i = 0; i < ns; ++i)
+        for (int k = i + 1; k < ns; ++k)
+            if (overlap(spans[i], spans[k]) && !(kind[i] == 0 && kind[k] == 0)) return AR_EALIAS;
+
+    *a = FusedArgs{};
+    a->in = in;
+    a->scratch = scratch;
+    a->out = out;
+    a->n = n;
+    a->L = slice_len_unit(P, n);
+    a->slot_words = 2 * ar_packet_slot_packets(P, n);
+    const int64_t chunk_words = (int64_t)kThreads * wpl;
+    a->chunks = (a->slot_words + chunk_words - 1) / chunk_words;
+    a->rank_lo = rank_lo;
+    a->nranks = rank_hi - rank_lo;
+    a->flag = flag;
+    bool al4 = true;
+    for (int p = 0; p < P; ++p) {
+        if (use_in) al4 = al4 && aligned_to(in.p[p], 4);
+        if (use_out) al4 = al4 && aligned_to(out.p[p], 4);
+    }
+    a->aligned4 = al4;
+    if (use_ctrl) {
+        a->status = static_cast<int32_t *>(ctrl);
+        a->epoch = static_cast<uint32_t *>(ctrl) + 1;
+        a->arrivals = static_cast<uint32_t *>(ctrl) + 2;
+    }
+    a->max_spins = max_spins ? max_spins : AR_DEFAULT_MAX_SPINS;
+    return AR_OK;
+}
+
+int packet_call(Kind kind, const ar_ptrs &in, const ar_ptrs &scratch, const ar_ptrs &out, int P,
+                int rank_lo, int rank_hi, int64_t n, uint32_t flag, void *ctrl, uint64_t max_spins,
+                void *stream) {
+    const bool use_in = kind == kFused || kind == kFusedEpoch || kind == kSend;
+    const bool use_out = kind == kFused || kind == kFusedEpoch || kind == kRecv;
+    const bool use_ctrl = kind != kSend;
+    // Two words per lane per chunk: 120.8 us against 125.1 us with one word
+    // for 512x7168 x 8 on MI355X (fewer, wider chunks; 134 VGPRs, 3
+    // workgroups per CU, which the sweep showed to be enough).
+    const int wpl = g_fused_wpl_override ? g_fused_wpl_override : 2;
+    FusedArgs a;
+    int rc = prepare_packet(in, scratch, out, use_in, use_out, use_ctrl, P, rank_lo, rank_hi, n,
+                            flag, kind != kFusedEpoch, ctrl, max_spins, wpl, &a);
+    if (rc != AR_OK || n == 0) return rc;
+    DeviceInfo dev;
+    if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
+    FusedKernel fn = wpl == 1 ? pick_p<1>(P, kind) : pick_p<2>(P, kind);
+
+    if (kind == kSend || kind == kRecvReduceSend || kind == kRecv) {
+        // Independent items, grid-stride; a modest grid leaves CUs free for a
+        // producer on another stream that a waiting phase depends on.
+        int64_t blocks = (int64_t)a.nranks * a.chunks;
+        if (blocks > (int64_t)dev.cus * 2) blocks = (int64_t)dev.cus * 2;
+        a.per_rank = 0;
+        return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, kThreads, a, stream);
+    }
+
+    // Persistent grid no larger than what is resident at once: B workgroups per
+    // rank, then B rebalanced so that every workgroup runs the same number of
+    // chunks.
+    const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(fn));
+    if (per_cu <= 0) return AR_ELAUNCH;
+    const int64_t resident = (int64_t)per_cu * dev.cus;
+    int64_t B = resident / a.nranks;
+    if (g_fused_per_rank_override > 0 && g_fused_per_rank_override < B)
+        B = g_fused_per_rank_override;
+    if (B > a.chunks) B = a.chunks;
+    if (B < 1) return AR_ELAUNCH;
+    const int64_t rounds = (a.chunks + B - 1) / B;
+    B = (a.chunks + rounds - 1) / rounds;
+    a.per_rank = (int)B;
+    return launch(reinterpret_cast<const void *>(fn), (unsigned)(B * a.nranks), kThreads, a,
+                  stream);
+}
 
 }  // namespace
 }  // namespace ar
@@ -327,83 +489,36 @@ int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void
 
 int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo, int rank_hi,
                     int64_t n, uint32_t flag, void *ctrl, uint64_t max_spins, void *stream) {
-    if (!valid_P(P) || n < 0 || flag == 0 || rank_lo < 0 || rank_hi > P || rank_lo >= rank_hi)
-        return AR_EINVAL;
-    if (!ctrl || !aligned_to(ctrl, 4)) return AR_EINVAL;
-    for (int p = 0; p < P; ++p) {
-        if (!in.p[p] || !out.p[p] || !scratch.p[p]) return AR_EINVAL;
-        if (!aligned_to(in.p[p], 2) || !aligned_to(out.p[p], 2) || !aligned_to(scratch.p[p], 16))
-            return AR_EINVAL;
-    }
-    if (n == 0) return AR_OK;
-    const int64_t sbytes = ar_packet_scratch_bytes(P, n);
-    // No two distinct buffers may share a byte (identical input pointers are
-    // fine: inputs are only read).
-    Span spans[3 * AR_MAX_P];
-    int kind[3 * AR_MAX_P];
-    int ns = 0;
-    for (int p = 0; p < P; ++p) {
-        spans[ns] = span_of(in.p[p], 0, n, 2);
-        kind[ns++] = 0;
-        spans[ns] = span_of(out.p[p], 0, n, 2);
-        kind[ns++] = 1;
-        spans[ns] = span_of(scratch.p[p], 0, sbytes, 1);
-        kind[ns++] = 2;
-    }
-    for (int i = 0; i < ns; ++i)
-        for (int k = i + 1; k < ns; ++k)
-            if (overlap(spans[i], spans[k]) && !(kind[i] == 0 && kind[k] == 0))
-                return AR_EALIAS;
-    const Span sc = span_of(ctrl, 0, AR_CTRL_BYTES, 1);
-    for (int i = 0; i < ns; ++i)
-        if (overlap(spans[i], sc)) return AR_EALIAS;
-
-    DeviceInfo dev;
-    if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
-    // Two words per lane per chunk: 120.8 us against 125.1 us with one word
-    // for 512x7168 x 8 on MI355X (fewer, wider chunks; 134 VGPRs, 3
-    // workgroups per CU, which the sweep showed to be enough).
-    const int wpl = g_fused_wpl_override ? g_fused_wpl_override : 2;
-    FusedKernel fn = pick_fused(P, wpl);
-    const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(fn));
-    if (per_cu <= 0) return AR_ELAUNCH;
-
-    FusedArgs a = {};
-    a.in = in;
-    a.scratch = scratch;
-    a.out = out;
-    a.n = n;
-    a.L = slice_len_unit(P, n);
-    a.slot_words = 2 * ar_packet_slot_packets(P, n);
-    const int64_t chunk_words = (int64_t)kThreads * wpl;
-    a.chunks = (a.slot_words + chunk_words - 1) / chunk_words;
-    a.rank_lo = rank_lo;
-    a.nranks = rank_hi - rank_lo;
-    a.flag = flag;
-    bool al4 = true;
-    for (int p = 0; p < P; ++p) al4 = al4 && aligned_to(in.p[p], 4) && aligned_to(out.p[p], 4);
-    a.aligned4 = al4;
-    a.status = static_cast<int32_t *>(ctrl);
-    a.max_spins = max_spins ? max_spins : AR_DEFAULT_MAX_SPINS;
-
-    // Persistent grid no larger than what is resident at once: B workgroups per
-    // rank, then B rebalanced so that every workgroup runs the same number of
-    // chunks.
-    const int64_t resident = (int64_t)per_cu * dev.cus;
-    int64_t B = resident / a.nranks;
-    if (g_fused_per_rank_override > 0 && g_fused_per_rank_override < B)
-        B = g_fused_per_rank_override;
-    if (B > a.chunks) B = a.chunks;
-    if (B < 1) return AR_ELAUNCH;
-    const int64_t rounds = (a.chunks + B - 1) / B;
-    B = (a.chunks + rounds - 1) / rounds;
-    a.per_rank = (int)B;
-    return launch(reinterpret_cast<const void *>(fn), (unsigned)(B * a.nranks), kThreads, a,
-                  stream);
+    return packet_call(kFused, in, scratch, out, P, rank_lo, rank_hi, n, flag, ctrl, max_spins,
+                       stream);
 }
 
-// Benchmark-only override of the fused kernel's workgroups per rank (0 = auto;
-// never above the resident limit).
+int ar_packet_fused_epoch(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo,
+                          int rank_hi, int64_t n, void *ctrl, uint64_t max_spins, void *stream) {
+    return packet_call(kFusedEpoch, in, scratch, out, P, rank_lo, rank_hi, n, 0, ctrl, max_spins,
+                       stream);
+}
+
+int ar_packet_send(ar_ptrs in, ar_ptrs scratch, int P, int rank_lo, int rank_hi, int64_t n,
+                   uint32_t flag, void *stream) {
+    return packet_call(kSend, in, scratch, ar_ptrs{}, P, rank_lo, rank_hi, n, flag, nullptr, 0,
+                       stream);
+}
+
+int ar_packet_recv_reduce_send(ar_ptrs scratch, int P, int rank_lo, int rank_hi, int64_t n,
+                               uint32_t flag, void *ctrl, uint64_t max_spins, void *stream) {
+    return packet_call(kRecvReduceSend, ar_ptrs{}, scratch, ar_ptrs{}, P, rank_lo, rank_hi, n, flag,
+                       ctrl, max_spins, stream);
+}
+
+int ar_packet_recv(ar_ptrs scratch, ar_ptrs out, int P, int rank_lo, int rank_hi, int64_t n,
+                   uint32_t flag, void *ctrl, uint64_t max_spins, void *stream) {
+    return packet_call(kRecv, ar_ptrs{}, scratch, out, P, rank_lo, rank_hi, n, flag, ctrl,
+                       max_spins, stream);
+}
+
+// Benchmark-only override of the packet kernels' workgroups per rank (0 =
+// auto; never above the resident limit) and words per lane per chunk.
 int ar_set_packet_tuning(int per_rank, int words_per_lane) {
     if (per_rank < 0 || !(words_per_lane == 0 || words_per_lane == 1 || words_per_lane == 2))
         return AR_EINVAL;

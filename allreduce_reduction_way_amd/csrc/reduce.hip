@@ -239,7 +239,24 @@ int ar_twoshot_share(ar_ptrs in, ar_ptrs out, int P, int rank, int64_t n, void *
     return launch_reduce(offset_ptrs(in, P, b), offset_ptrs(out, P, b), P, true, e - b, stream);
 }
 
-// Benchmark-only launch-shape override for the three entry points above.
+int ar_reduce_scatter_share(ar_ptrs in, void *out, int P, int rank, int64_t recvcount,
+                            void *stream) {
+    const void *outs[1] = {out};
+    int rc = check_buffers(in, outs, 1, P, recvcount);
+    if (rc != AR_OK) return rc;
+    if (rank < 0 || rank >= P) return AR_EINVAL;
+    const int64_t begin = (int64_t)rank * recvcount;
+    // the output may be exactly this rank's own block of an input (in place)
+    for (int p = 0; p < P; ++p)
+        if (partial_overlap(span_of(out, 0, recvcount, 2), span_of(in.p[p], begin, recvcount, 2)))
+            return AR_EALIAS;
+    if (recvcount == 0) return AR_OK;
+    ar_ptrs o = {};
+    o.p[0] = out;
+    return launch_reduce(offset_ptrs(in, P, begin), o, P, false, recvcount, stream);
+}
+
+// Benchmark-only launch-shape override for the reduce entry points above.
 int ar_set_reduce_tuning(int unroll, int threads, int max_blocks) {
     if (!(unroll == 0 || unroll == 1 || unroll == 2 || unroll == 4) || max_blocks < 0 ||
         !(threads == 0 || threads == 64 || threads == 128 || threads == 256))

@@ -33,5 +33,16 @@ TWOSHOT_680x5120_R3 = Workload("twoshot_680x5120_p8_rank3", "twoshot_share", 8, 
 TWOSHOT_64Mi_P4 = Workload("twoshot_64Mi_p4_all_owners", "twoshot_share", 4, 64 * 1024 * 1024,
                            "normal", ranks=(0, 1, 2, 3))
 
-ALL = (ONESHOT_4K, WRITE_BCAST_440x5120, PACKET_512x7168, TWOSHOT_680x5120_R3, TWOSHOT_64Mi_P4)
+# Widened rows: the unfused three-operation packet decomposition, the fused
+# packet kernel with its flag on the device replayed from a HIP graph, and the
+# one-shot reduce-scatter sibling (rank 3's block of 440x5120 x 8).
+PACKET_3OP_512x7168 = Workload("packet_3op_512x7168_p8", "packet_3op", 8, 512 * 7168, "uniform",
+                               ranks=tuple(range(8)), calls=3)
+PACKET_EPOCH_GRAPH_512x7168 = Workload("packet_epoch_graph_512x7168_p8", "packet_epoch", 8,
+                                       512 * 7168, "uniform", ranks=tuple(range(8)), calls=3)
+REDUCE_SCATTER_440x5120_R3 = Workload("reduce_scatter_440x5120_p8_rank3", "reduce_scatter", 8,
+                                      440 * 5120, "uniform", ranks=(3,))
+
+ALL = (ONESHOT_4K, WRITE_BCAST_440x5120, PACKET_512x7168, TWOSHOT_680x5120_R3, TWOSHOT_64Mi_P4,
+       PACKET_3OP_512x7168, PACKET_EPOCH_GRAPH_512x7168, REDUCE_SCATTER_440x5120_R3)
 BY_NAME = {w.name: w for w in ALL}

@@ -136,21 +136,73 @@ def make_rows(names, torch, ar, I, W, stream):
 
         rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, len(w.ranks), owners,
                            "4 owner launches per step, full buffer into 4 outputs")
+    if W.PACKET_3OP_512x7168.name in names:
+        w = W.PACKET_3OP_512x7168
+        ins = dev_inputs(w)
+        nb = ar.ar_packet_scratch_bytes(w.P, w.n)
+        scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
+        outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
+        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        state3 = {"flag": 0}
+
+        def three_op(i, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl, st=state3, n=w.n):
+            st["flag"] += 1
+            ar.ar_packet_send(ins, scratch, st["flag"], stream=stream)
+            ar.ar_packet_recv_reduce_send(scratch, n, st["flag"], ctrl, stream=stream)
+            ar.ar_packet_recv(scratch, outs, st["flag"], ctrl, stream=stream)
+
+        row = Row(w.name, 20 * w.n * w.P, 3, three_op,
+                  "send -> recv-reduce-send -> recv, one launch each; same bytes as fused")
+        row.ctrl = ctrl
+        rows[w.name] = row
+    if W.PACKET_EPOCH_GRAPH_512x7168.name in names:
+        w = W.PACKET_EPOCH_GRAPH_512x7168
+        ins = dev_inputs(w)
+        nb = ar.ar_packet_scratch_bytes(w.P, w.n)
+        scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
+        outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
+        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        ar.ar_packet_fused_epoch(ins, scratch, outs, ctrl, stream=stream)  # warm-up, flag 1
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            ar.ar_packet_fused_epoch(ins, scratch, outs, ctrl)
+        torch.cuda.synchronize()
+
+        def replay(i, graph=graph):
+            graph.replay()
+
+        row = Row(w.name, 20 * w.n * w.P, 1, replay,
+                  "fused kernel, flag = device epoch + 1, replayed from a HIP graph")
+        row.ctrl = ctrl
+        rows[w.name] = row
+    if W.REDUCE_SCATTER_440x5120_R3.name in names:
+        w = W.REDUCE_SCATTER_440x5120_R3
+        ins = dev_inputs(w)
+        rc = w.n // w.P
+        out = torch.empty(rc, dtype=torch.int16, device=dev)
+        rows[w.name] = Row(w.name, (w.P + 1) * rc * 2, 1,
+                           lambda i, ins=ins, out=out, rc=rc: ar.ar_reduce_scatter_share(
+                               ins, out, 3, rc, stream=stream),
+                           "rank 3's block: read P x block, write 1 x block")
     return rows
 
 
 # ----------------------------------------------------------------------- timing
 
 def time_streamed(torch, stream, fn, steps, warmup):
-    for i in range(warmup):
-        fn(i)
+    # `stream` is also made current, so graph replays land on it too
+    with torch.cuda.stream(stream):
+        for i in range(warmup):
+            fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(steps):
-        fn(warmup + i)
-    e1.record(stream)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for i in range(steps):
+            fn(warmup + i)
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return e0.elapsed_time(e1) / steps, wall
@@ -160,14 +212,14 @@ def time_per_call(torch, stream, fn, calls, scrub=None):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(calls)]
     for i, (a, b) in enumerate(evs):
-        if scrub is not None:
-            # read-only scrub: streams 512 MiB through L2 and the MALL, evicting
-            # the workload's lines without leaving dirty data behind
-            with torch.cuda.stream(stream):
+        with torch.cuda.stream(stream):
+            if scrub is not None:
+                # read-only scrub: streams 512 MiB through L2 and the MALL,
+                # evicting the workload's lines without leaving dirty data
                 scrub.view(torch.int32).amax()
-        a.record(stream)
-        fn(i)
-        b.record(stream)
+            a.record(stream)
+            fn(i)
+            b.record(stream)
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in evs)
     return {"mean_us": 1e3 * sum(ms) / len(ms), "median_us": 1e3 * ms[len(ms) // 2],

@@ -59,15 +59,22 @@ enum ar_status {
 
 /*
  * Device control block of the packet kernels: 64 bytes of device memory the
- * caller allocates and zeroes once.  `status` is AR_OK until a kernel's
- * bounded wait runs out; the first waiter to time out stores AR_ETIMEDOUT and
- * every waiter of that launch then stops waiting.  The library never clears
- * it: the caller reads it back (e.g. after synchronising) and re-zeroes it.
+ * caller allocates and zeroes once.
+ *   status    AR_OK until a kernel's bounded wait runs out; the first waiter to
+ *             time out stores AR_ETIMEDOUT and every waiter that polls the
+ *             block afterwards stops waiting.  The library never clears it:
+ *             the caller reads it back (after synchronising) and re-zeroes it.
+ *   epoch     the flag of the last completed ar_packet_fused_epoch call on
+ *             this block (the next call uses epoch + 1).
+ *   arrivals  workgroups of the running ar_packet_fused_epoch launch that
+ *             have finished; back to 0 when the launch completes.
  */
 #define AR_CTRL_BYTES 64
 typedef struct ar_ctrl {
     int32_t status;
-    uint32_t reserved[15];
+    uint32_t epoch;
+    uint32_t arrivals;
+    uint32_t reserved[13];
 } ar_ctrl;
 
 /* Default bound on the polls of one packet word (0 passed as max_spins). */
@@ -112,6 +119,21 @@ int ar_oneshot_write_bcast(ar_ptrs in, ar_ptrs out, int P, int64_t n, void *stre
  *   in, out, P as for ar_oneshot_write_bcast; rank in [0, P).
  * ------------------------------------------------------------------------- */
 int ar_twoshot_share(ar_ptrs in, ar_ptrs out, int P, int rank, int64_t n, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * ar_reduce_scatter_share -- one-shot reduce-scatter share of `rank`: each
+ * input holds P blocks of `recvcount` elements and the rank keeps the sum of
+ * its own block, out[i] = sum_p in.p[p][rank * recvcount + i].  The same
+ * push-reduce kernel serves reduce-scatter with a per-peer source stride of
+ * recvcount and an owner offset of rank * recvcount, allreduce with both 0
+ * (torchcomms PR #3850, commit summary D117629707).
+ *   in    P inputs of P * recvcount bf16.
+ *   out   recvcount bf16; may be exactly the rank's own block of an input
+ *         (in place); any other overlap with an input block read is AR_EALIAS.
+ *   rank  in [0, P).
+ * ------------------------------------------------------------------------- */
+int ar_reduce_scatter_share(ar_ptrs in, void *out, int P, int rank, int64_t recvcount,
+                            void *stream);
 
 /* ---------------------------------------------------------------------------
  * LL packets.  Data and flag travel in one packet so that arrival is read off
@@ -176,6 +198,41 @@ int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void
  * ------------------------------------------------------------------------- */
 int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo, int rank_hi,
                     int64_t n, uint32_t flag, void *ctrl, uint64_t max_spins, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * ar_packet_fused_epoch -- ar_packet_fused whose flag lives in the control
+ * block instead of the argument list: the call uses flag = ctrl->epoch + 1,
+ * read on the device, and its last workgroup stores that flag back as the new
+ * epoch.  A launch captured into a HIP graph therefore rotates its flag on
+ * every replay, where a by-value flag would be baked in at capture and every
+ * stale packet would already match it (torchcomms PR #3850, PR summary,
+ * hazard G2).  Same buffers and rules as ar_packet_fused; the first call on a
+ * zeroed control block uses flag 1.  A rank range split over several launches
+ * gives each launch its own control block: their epochs advance together as
+ * long as every launch takes part in every call.
+ * ------------------------------------------------------------------------- */
+int ar_packet_fused_epoch(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo,
+                          int rank_hi, int64_t n, void *ctrl, uint64_t max_spins, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * The three-operation packet decomposition that the fused kernel replaces
+ * (ARK PR #254, description: send_packet -> recv_reduce_send_packet ->
+ * recv_packet, one launch per phase).  Same scratch layout, flags and results
+ * as ar_packet_fused; for ranks [rank_lo, rank_hi):
+ *   ar_packet_send              scatter: in.p[r][slice j] -> inbox_j[slot r]
+ *   ar_packet_recv_reduce_send  wait for inbox_r[slot 0..P-1], sum in rank
+ *                               order, broadcast into resbox_j[slot r]
+ *   ar_packet_recv              wait for resbox_r[slot 0..P-1], decode into
+ *                               out.p[r]
+ * Launched in this order on one stream they reproduce ar_packet_fused bit for
+ * bit.  Waits are bounded and report through ctrl like the fused kernel.
+ * ------------------------------------------------------------------------- */
+int ar_packet_send(ar_ptrs in, ar_ptrs scratch, int P, int rank_lo, int rank_hi, int64_t n,
+                   uint32_t flag, void *stream);
+int ar_packet_recv_reduce_send(ar_ptrs scratch, int P, int rank_lo, int rank_hi, int64_t n,
+                               uint32_t flag, void *ctrl, uint64_t max_spins, void *stream);
+int ar_packet_recv(ar_ptrs scratch, ar_ptrs out, int P, int rank_lo, int rank_hi, int64_t n,
+                   uint32_t flag, void *ctrl, uint64_t max_spins, void *stream);
 
 /* ---------------------------------------------------------------------------
  * Host-only helpers: no GPU needed, no HIP call made.

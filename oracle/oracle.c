@@ -152,6 +152,21 @@ int orc_twoshot_share(const uint16_t *const *x, int P, int64_t n, int r, uint16_
     return ORC_OK;
 }
 
+/* ---- one-shot reduce-scatter -------------------------------------------- */
+
+/* Each input holds P blocks of rc elements; rank r keeps the rank-order sum of
+ * block r: the reduce-scatter case of the one-shot push-reduce kernel, with a
+ * per-peer source stride of rc and an owner offset of r * rc (torchcomms PR
+ * #3850, commit summary D117629707). */
+int orc_reduce_scatter(const uint16_t *const *x, int P, int64_t rc, int r, uint16_t *y)
+{
+    if (!fp_env_ok()) return ORC_EFPENV;
+    if (P < 1 || rc < 0 || r < 0 || r >= P || !x || (rc > 0 && !y)) return ORC_EINVAL;
+    for (int64_t i = 0; i < rc; ++i)
+        y[i] = f32_to_bf16_rne(sum_in_rank_order(x, P, (int64_t)r * rc + i));
+    return ORC_OK;
+}
+
 /* ---- LL packets --------------------------------------------------------- */
 
 int64_t orc_ll_packets(int64_t n)

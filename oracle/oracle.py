@@ -36,6 +36,7 @@ def _load():
             "orc_write_bcast": (i32, [P16, i32, i64, P16]),
             "orc_slice": (i32, [i32, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]),
             "orc_twoshot_share": (i32, [P16, i32, i64, i32, P16]),
+            "orc_reduce_scatter": (i32, [P16, i32, i64, i32, vp]),
             "orc_ll_packets": (i64, [i64]),
             "orc_ll_encode": (i32, [vp, i64, u32, vp]),
             "orc_ll_decode": (i32, [vp, i64, u32, vp]),
@@ -103,6 +104,19 @@ def twoshot_share(xs, r: int, prior_outs) -> list:
     q, k2 = _ptrs(outs)
     _check(_load().orc_twoshot_share(p, len(xs), n, r, q), "orc_twoshot_share")
     return outs
+
+
+def reduce_scatter(xs, r: int) -> np.ndarray:
+    """Rank r's block of the sum: each input holds P blocks of n / P elements."""
+    xs, n = _as_inputs(xs)
+    P = len(xs)
+    if n % P:
+        raise ValueError("reduce-scatter inputs hold P equal blocks")
+    rc = n // P
+    y = np.empty(rc, dtype=np.uint16)
+    p, keep = _ptrs(xs)
+    _check(_load().orc_reduce_scatter(p, P, rc, r, y.ctypes.data), "orc_reduce_scatter")
+    return y
 
 
 def ll_packets(n: int) -> int:

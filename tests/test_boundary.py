@@ -187,3 +187,42 @@ def test_tuning_validation():
     assert _err(ar.ar_set_packet_tuning, 0, 3) == ar.AR_EINVAL
     ar.ar_set_reduce_tuning(0, 0, 0)
     ar.ar_set_packet_tuning(0, 0)
+
+
+def test_reduce_scatter_validation():
+    ins = _bufs(8)
+    out = FAKE + (1 << 31)
+    for rank in (-1, 8):
+        assert _err(ar.ar_reduce_scatter_share, ins, out, rank, recvcount=64,
+                    stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_reduce_scatter_share, ins, out, 0, recvcount=-1, stream=STREAM) == ar.AR_EINVAL
+    # output 2 elements into rank 3's block of input 5: partial overlap
+    assert _err(ar.ar_reduce_scatter_share, ins, ins[5] + 2 * (3 * 64 + 2), 3, recvcount=64,
+                stream=STREAM) == ar.AR_EALIAS
+    ar.ar_reduce_scatter_share(ins, out, 3, recvcount=0, stream=STREAM)
+
+
+def test_packet_phase_and_epoch_validation():
+    P, n = 8, 4096
+    ins = _bufs(P)
+    outs = _bufs(P, base=FAKE + (1 << 30))
+    scr = _bufs(P, base=FAKE + (1 << 31))
+    ctrl = FAKE + (3 << 30)
+    assert _err(ar.ar_packet_send, ins, scr, 0, n=n, stream=STREAM) == ar.AR_EINVAL        # flag 0
+    assert _err(ar.ar_packet_recv_reduce_send, scr, n, 1, 0, stream=STREAM) == ar.AR_EINVAL  # ctrl
+    assert _err(ar.ar_packet_recv_reduce_send, scr, n, 0, ctrl, stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_packet_recv, scr, outs, 1, 0, n=n, stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_packet_fused_epoch, ins, scr, outs, 0, n=n, stream=STREAM) == ar.AR_EINVAL
+    bad = list(scr)
+    bad[2] = scr[1] + 64                                                                   # overlap
+    assert _err(ar.ar_packet_send, ins, bad, 1, n=n, stream=STREAM) == ar.AR_EALIAS
+    assert _err(ar.ar_packet_recv, scr, [scr[0]] + outs[1:], 1, ctrl, n=n,
+                stream=STREAM) == ar.AR_EALIAS
+    assert _err(ar.ar_packet_fused_epoch, ins, scr, outs, scr[0] + 128, n=n,
+                stream=STREAM) == ar.AR_EALIAS
+    for fn, args in [(ar.ar_packet_send, (ins, scr, 1)),
+                     (ar.ar_packet_recv_reduce_send, (scr, 0, 1, ctrl)),
+                     (ar.ar_packet_recv, (scr, outs, 1, ctrl)),
+                     (ar.ar_packet_fused_epoch, (ins, scr, outs, ctrl))]:
+        kw = {} if fn is ar.ar_packet_recv_reduce_send else {"n": 0}
+        fn(*args, stream=STREAM, **kw)                                                   # no-ops

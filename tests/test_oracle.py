@@ -293,3 +293,33 @@ def test_packet_scratch_size_for_512x7168():
     # 114688 packets per slot, 2 boxes x 8 slots x 114688 x 16 B per rank.
     assert O.packet_slot_packets(8, 512 * 7168) == 114688
     assert O.packet_scratch_bytes(8, 512 * 7168) == 29360128
+
+
+# ------------------------------------------------------------ reduce-scatter
+
+@pytest.mark.parametrize("P", [2, 3, 8])
+def test_reduce_scatter_closed_form(P):
+    rc = 100
+    xs = [np.full(P * rc, 0x3F80, np.uint16)] * P
+    expected = {2: 0x4000, 3: 0x4040, 8: 0x4100}[P]
+    for r in range(P):
+        assert (O.reduce_scatter(xs, r) == expected).all()
+
+
+@pytest.mark.parametrize("P", [2, 4, 8])
+def test_reduce_scatter_against_exact_rational_model(P):
+    rng = np.random.default_rng(77 + P)
+    rc = 16
+    xs = [_random_bf16(rng, P * rc, "narrow") for _ in range(P)]
+    for r in range(P):
+        y = O.reduce_scatter(xs, r)
+        for i in range(rc):
+            assert int(y[i]) == E.reduce_element([int(x[r * rc + i]) for x in xs]), (r, i)
+
+
+def test_reduce_scatter_blocks_tile_the_oneshot_sum():
+    P, rc = 8, 1000
+    xs = I.make_inputs("uniform", P, P * rc, seed=9)
+    y = O.oneshot_sum(xs)
+    blocks = [O.reduce_scatter(xs, r) for r in range(P)]
+    assert np.array_equal(np.concatenate(blocks), y)
