@@ -14,6 +14,7 @@ PKG = pathlib.Path(__file__).resolve().parent
 ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libar.so"
+RESOURCES = PKG / "libar.resources.txt"   # per-kernel register/scratch report of the last build
 SOURCES = ["host.hip", "reduce.hip", "packet.hip"]
 
 HIPCC_FLAGS = [
@@ -26,18 +27,23 @@ HIPCC_FLAGS = [
 
 def build(verbose: bool = False) -> pathlib.Path:
     tmp = LIB.with_suffix(".so.tmp")
-    cmd = ["hipcc", *HIPCC_FLAGS, f"-I{ROOT / 'include'}", f"-I{CSRC}",
-           *[str(CSRC / s) for s in SOURCES], "-o", str(tmp)]
+    cmd = ["hipcc", *HIPCC_FLAGS, "-Rpass-analysis=kernel-resource-usage",
+           f"-I{ROOT / 'include'}", f"-I{CSRC}", *[str(CSRC / s) for s in SOURCES], "-o", str(tmp)]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
-    msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
+    lines = (res.stdout + res.stderr).splitlines()
+    report = [l.split("remark: ", 1)[1].replace(" [-Rpass-analysis=kernel-resource-usage]", "")
+              for l in lines if "remark: " in l and "kernel-resource-usage" in l]
+    msgs = [l for l in lines if noise not in l and "kernel-resource-usage" not in l
+            and not l.startswith(" ") and l.strip() != "|"]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
     tmp.replace(LIB)
+    RESOURCES.write_text("\n".join(report) + "\n")
     return LIB
 
 

@@ -123,8 +123,9 @@ __device__ __forceinline__ int64_t slice_len(const FusedArgs &a, int j, int P) {
 // covers loads and stores alike, so a load issued after a write-through store
 // would also wait for that store's acknowledgement.
 template <int P, int WPL>
-__device__ __forceinline__ bool pipeline_step(const FusedArgs &a, int r, bool do_s, int64_t cs,
-                                              bool do_r, int64_t cr, bool do_v, int64_t cv) {
+__device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag, int r, bool do_s,
+                                              int64_t cs, bool do_r, int64_t cr, bool do_v,
+                                              int64_t cv) {
     const uint16_t *x_r = static_cast<const uint16_t *>(a.in.p[r]);
     const uint64_t *mine = static_cast<const uint64_t *>(a.scratch.p[r]);
     constexpr int64_t CW = (int64_t)kThreads * WPL;
@@ -163,7 +164,7 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, int r, bool do
             for (int k = 0; k < WPL; ++k) {
                 const int64_t w = wv0 + k * kThreads;
                 vv[s][k] = 2 * w < len ? load_word(mine + (int64_t)(P + s) * a.slot_words + w)
-                                       : make_word(0, a.flag);
+                                       : make_word(0, flag);
             }
         }
     }
@@ -177,7 +178,7 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, int r, bool do
 #pragma unroll
             for (int k = 0; k < WPL; ++k) {
                 const int64_t w = ws0 + k * kThreads;
-                if (w < words) store_word(slot + w, make_word(d[j][k], a.flag));
+                if (w < words) store_word(slot + w, make_word(d[j][k], flag));
             }
         }
     }
@@ -191,13 +192,13 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, int r, bool do
             uint32_t dw[P];
 #pragma unroll
             for (int s = 0; s < P; ++s) {
-                if (word_flag(vr[k][s]) != a.flag &&
-                    !wait_word(mine + (int64_t)s * a.slot_words + w, a.flag, vr[k][s], a.status,
+                if (word_flag(vr[k][s]) != flag &&
+                    !wait_word(mine + (int64_t)s * a.slot_words + w, flag, vr[k][s], a.status,
                                a.max_spins))
                     return false;
                 dw[s] = word_data(vr[k][s]);
             }
-            const uint64_t res = make_word(reduce_word<P>(dw), a.flag);
+            const uint64_t res = make_word(reduce_word<P>(dw), flag);
 #pragma unroll
             for (int j = 0; j < P; ++j)
                 store_word(static_cast<uint64_t *>(a.scratch.p[j]) + (int64_t)(P + r) * a.slot_words +
@@ -216,8 +217,8 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, int r, bool do
             for (int k = 0; k < WPL; ++k) {
                 const int64_t w = wv0 + k * kThreads;
                 if (2 * w >= len) continue;
-                if (word_flag(vv[s][k]) != a.flag &&
-                    !wait_word(mine + (int64_t)(P + s) * a.slot_words + w, a.flag, vv[s][k],
+                if (word_flag(vv[s][k]) != flag &&
+                    !wait_word(mine + (int64_t)(P + s) * a.slot_words + w, flag, vv[s][k],
                                a.status, a.max_spins))
                     return false;
                 store_pair(out_r + s * a.L, 2 * w, len, a.aligned4, word_data(vv[s][k]));
@@ -244,15 +245,18 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, int r, bool do
 // count completes only after the last one has, so all of them use one flag.
 template <int P, int WPL, bool EPOCH>
 __global__ __launch_bounds__(kThreads) void k_packet_fused(FusedArgs a) {
-    if (EPOCH) {
-        a.flag = __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    }
+    // The arguments stay read-only (writing to them would move the whole
+    // struct to scratch memory); the epoch is made wave-uniform.
+    const uint32_t flag =
+        EPOCH ? __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u)
+              : a.flag;
     const int r = a.rank_lo + (int)(blockIdx.x % (unsigned)a.nranks);
     const int64_t m = blockIdx.x / (unsigned)a.nranks;
     const int64_t B = a.per_rank;
     const int64_t mine = m < a.chunks ? (a.chunks - 1 - m) / B + 1 : 0;
     for (int64_t i = 0; i < mine + 2; ++i) {
-        if (!pipeline_step<P, WPL>(a, r, i < mine, m + i * B, i >= 1 && i <= mine,
+        if (!pipeline_step<P, WPL>(a, flag, r, i < mine, m + i * B, i >= 1 && i <= mine,
                                    m + (i - 1) * B, i >= 2, m + (i - 2) * B))
             break;
     }
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(kThreads) void k_packet_fused(FusedArgs a) {
                                                            __HIP_MEMORY_SCOPE_AGENT);
             if (before == gridDim.x - 1) {
                 __hip_atomic_store(a.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(a.epoch, a.flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(a.epoch, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
@@ -281,7 +285,8 @@ __global__ __launch_bounds__(kThreads) void k_packet_phase(FusedArgs a) {
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int r = a.rank_lo + (int)(it % a.nranks);
         const int64_t c = it / a.nranks;
-        if (!pipeline_step<P, WPL>(a, r, PHASE == 0, c, PHASE == 1, c, PHASE == 2, c)) return;
+        if (!pipeline_step<P, WPL>(a, a.flag, r, PHASE == 0, c, PHASE == 1, c, PHASE == 2, c))
+            return;
     }
 }
 

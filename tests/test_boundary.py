@@ -226,3 +226,25 @@ def test_packet_phase_and_epoch_validation():
                      (ar.ar_packet_fused_epoch, (ins, scr, outs, ctrl))]:
         kw = {} if fn is ar.ar_packet_recv_reduce_send else {"n": 0}
         fn(*args, stream=STREAM, **kw)                                                   # no-ops
+
+
+def test_no_kernel_uses_scratch_memory():
+    """Every kernel of the last build keeps its state in registers: a kernel
+    that spills or moves its argument block to scratch memory is a
+    performance bug (the build records the compiler's resource report)."""
+    report = ar.LIB_PATH.with_name("libar.resources.txt")
+    if not report.exists():
+        pytest.skip("no resource report: the library was built without it")
+    kernels, current = {}, None
+    for line in report.read_text().splitlines():
+        line = line.strip()
+        if line.startswith("Function Name:"):
+            current = line.split(":", 1)[1].strip()
+            kernels[current] = {}
+        elif current and ":" in line:
+            k, v = line.split(":", 1)
+            kernels[current][k.strip()] = v.strip()
+    assert len(kernels) >= 50
+    bad = {k: v.get("ScratchSize [bytes/lane]") for k, v in kernels.items()
+           if v.get("ScratchSize [bytes/lane]") != "0" or v.get("VGPRs Spill") != "0"}
+    assert not bad, bad
