@@ -122,10 +122,19 @@ __device__ __forceinline__ int64_t slice_len(const FusedArgs &a, int j, int P) {
 // the step is issued before any store: on CDNA the vector-memory counter
 // covers loads and stores alike, so a load issued after a write-through store
 // would also wait for that store's acknowledgement.
-template <int P, int WPL>
+//
+// CARRY: the rank's own contributions come from registers instead of being
+// read back from its own slots -- its scatter of chunk c into inbox_r[slot r]
+// (one step before it reduces c) and its broadcast of chunk c into
+// resbox_r[slot r] (one step before it receives c).  The packets are still
+// written, so the scratch image is unchanged; only the read-back of the own
+// slot, a local memory access, goes away.  `own_d` carries the scatter data
+// and `own_res` the reduced words from one step to the next.
+template <int P, int WPL, bool CARRY>
 __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag, int r, bool do_s,
                                               int64_t cs, bool do_r, int64_t cr, bool do_v,
-                                              int64_t cv) {
+                                              int64_t cv, uint32_t (&own_d)[WPL],
+                                              uint32_t (&own_res)[WPL]) {
     const uint16_t *x_r = static_cast<const uint16_t *>(a.in.p[r]);
     const uint64_t *mine = static_cast<const uint64_t *>(a.scratch.p[r]);
     constexpr int64_t CW = (int64_t)kThreads * WPL;
@@ -152,8 +161,12 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag,
         for (int k = 0; k < WPL; ++k) {
             const int64_t w = wr0 + k * kThreads;
 #pragma unroll
-            for (int s = 0; s < P; ++s)
-                vr[k][s] = w < r_words ? load_word(mine + (int64_t)s * a.slot_words + w) : 0;
+            for (int s = 0; s < P; ++s) {
+                if (CARRY && s == r)
+                    vr[k][s] = make_word(own_d[k], flag);
+                else
+                    vr[k][s] = w < r_words ? load_word(mine + (int64_t)s * a.slot_words + w) : 0;
+            }
         }
     }
     if (do_v) {
@@ -163,8 +176,11 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag,
 #pragma unroll
             for (int k = 0; k < WPL; ++k) {
                 const int64_t w = wv0 + k * kThreads;
-                vv[s][k] = 2 * w < len ? load_word(mine + (int64_t)(P + s) * a.slot_words + w)
-                                       : make_word(0, flag);
+                if (CARRY && s == r)
+                    vv[s][k] = make_word(own_res[k], flag);
+                else
+                    vv[s][k] = 2 * w < len ? load_word(mine + (int64_t)(P + s) * a.slot_words + w)
+                                           : make_word(0, flag);
             }
         }
     }
@@ -184,10 +200,12 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag,
     }
 
     // ---- reduce inbox_r[slot 0..P-1] in rank order, broadcast to resbox_j[slot r]
+    uint32_t res_d[WPL];
     if (do_r) {
 #pragma unroll
         for (int k = 0; k < WPL; ++k) {
             const int64_t w = wr0 + k * kThreads;
+            res_d[k] = 0;
             if (w >= r_words) continue;
             uint32_t dw[P];
 #pragma unroll
@@ -198,7 +216,8 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag,
                     return false;
                 dw[s] = word_data(vr[k][s]);
             }
-            const uint64_t res = make_word(reduce_word<P>(dw), flag);
+            res_d[k] = reduce_word<P>(dw);
+            const uint64_t res = make_word(res_d[k], flag);
 #pragma unroll
             for (int j = 0; j < P; ++j)
                 store_word(static_cast<uint64_t *>(a.scratch.p[j]) + (int64_t)(P + r) * a.slot_words +
@@ -223,6 +242,15 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag,
                     return false;
                 store_pair(out_r + s * a.L, 2 * w, len, a.aligned4, word_data(vv[s][k]));
             }
+        }
+    }
+
+    // hand this step's own-slot words to the next step
+    if (CARRY) {
+#pragma unroll
+        for (int k = 0; k < WPL; ++k) {
+            if (do_r) own_res[k] = res_d[k];
+            if (do_s) own_d[k] = d[r][k];
         }
     }
     return true;
@@ -255,9 +283,10 @@ __global__ __launch_bounds__(kThreads) void k_packet_fused(FusedArgs a) {
     const int64_t m = blockIdx.x / (unsigned)a.nranks;
     const int64_t B = a.per_rank;
     const int64_t mine = m < a.chunks ? (a.chunks - 1 - m) / B + 1 : 0;
+    uint32_t own_d[WPL] = {}, own_res[WPL] = {};
     for (int64_t i = 0; i < mine + 2; ++i) {
-        if (!pipeline_step<P, WPL>(a, flag, r, i < mine, m + i * B, i >= 1 && i <= mine,
-                                   m + (i - 1) * B, i >= 2, m + (i - 2) * B))
+        if (!pipeline_step<P, WPL, true>(a, flag, r, i < mine, m + i * B, i >= 1 && i <= mine,
+                                         m + (i - 1) * B, i >= 2, m + (i - 2) * B, own_d, own_res))
             break;
     }
     if (EPOCH) {
@@ -285,7 +314,9 @@ __global__ __launch_bounds__(kThreads) void k_packet_phase(FusedArgs a) {
     for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int r = a.rank_lo + (int)(it % a.nranks);
         const int64_t c = it / a.nranks;
-        if (!pipeline_step<P, WPL>(a, a.flag, r, PHASE == 0, c, PHASE == 1, c, PHASE == 2, c))
+        uint32_t unused_d[WPL], unused_res[WPL];
+        if (!pipeline_step<P, WPL, false>(a, a.flag, r, PHASE == 0, c, PHASE == 1, c, PHASE == 2,
+                                          c, unused_d, unused_res))
             return;
     }
 }

@@ -259,3 +259,27 @@ def test_packet_fused_every_launch_shape(per_rank, wpl, P, n):
     got = _images(scratch)
     for r in range(P):
         assert np.array_equal(got[r], img2[r])
+
+
+def test_packet_fused_fifty_calls_rotating_flags():
+    """Fifty consecutive calls on one scratch set, inputs changing every call:
+    each call's outputs are checked, and the full scratch image on a few."""
+    P, n = 8, 8192 * 9 + 1
+    scratch = _scratch(P, n)
+    images = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    ctrl = ctrl_block()
+    outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    announce("packet fused: 50 calls, flags 1..50")
+    for call in range(50):
+        f = call + 1
+        xs = I.make_inputs("uniform", P, n, seed=100 + call)
+        ar.ar_packet_fused([to_dev(x) for x in xs], scratch, outs, f, ctrl)
+        torch.cuda.synchronize()
+        assert ctrl_status(ctrl) == 0, call
+        want, images = O.packet_fused(xs, f, images)
+        for r in range(P):
+            assert np.array_equal(to_host(outs[r]), want[r]), (call, r)
+        if call in (0, 17, 49):
+            got = _images(scratch)
+            for r in range(P):
+                assert np.array_equal(got[r], images[r]), (call, r)
