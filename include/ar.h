@@ -190,9 +190,13 @@ int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void
  *   flag     != 0, strictly increasing from call to call on one scratch set
  *            (call c uses flag c + 1).  Wrap-around is not supported.
  *   ctrl     control block (AR_CTRL_BYTES), required.
- * A range covering fewer than all P ranks only completes if the packets of
- * the other ranks for this flag are already in place (e.g. staged with
- * ar_ll_encode); otherwise it times out and reports AR_ETIMEDOUT.  Inputs,
+ * A range covering fewer than all P ranks completes once the packets of the
+ * other ranks for this flag are in place: staged before (e.g. with
+ * ar_ll_encode or an earlier launch on the same stream) or written by a launch
+ * that runs at the same time.  HIP does not promise that launches on two
+ * streams of one process run at the same time (streams share a few hardware
+ * queues), so a launch that waits on one queued after it may end in
+ * AR_ETIMEDOUT instead; it never hangs.  Inputs,
  * outputs and scratch buffers must not overlap each other (AR_EALIAS).  Two
  * calls in flight on one scratch set are not allowed.
  * ------------------------------------------------------------------------- */

@@ -207,30 +207,43 @@ def test_packet_zeroed_scratch_single_rank_times_out():
     assert ctrl_status(ctrl) == ar.AR_ETIMEDOUT
 
 
-def test_packet_split_launch_with_skewed_producers():
-    """Ranks 0..3 and 4..7 launched on two streams, the second after a host
-    sleep: the first launch's waits span the skew and complete."""
+def test_packet_split_launch_on_one_stream_with_staged_second_half():
+    """Ranks 0..3 run in one launch against ranks 4..7's packets staged from
+    the oracle's image, then ranks 4..7 run in a second launch on the same
+    stream: both halves complete and together give the full result (two
+    launches that wait on each other would need two concurrently running
+    streams, which HIP does not guarantee)."""
     P, n = 8, 8192 * 5 + 9
     xs = I.make_inputs("uniform", P, n, seed=12)
-    d_in = [to_dev(x) for x in xs]
-    scratch = _scratch(P, n)
+    zero = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    want, full = O.packet_fused(xs, 1, zero)
+    staged = zero
+    for r in range(4, 8):   # keep only ranks 4..7's packets
+        staged = [np.where(_rank_mask(P, n, r), f_, s_) for f_, s_ in zip(full, staged)]
+    scratch = _scratch(P, n, staged)
     outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
-    ctrl_a, ctrl_b = ctrl_block(), ctrl_block()
-    s_a, s_b = torch.cuda.Stream(), torch.cuda.Stream()
+    ctrl = ctrl_block()
+    d_in = [to_dev(x) for x in xs]
+    announce("packet split launch: ranks 0..3 against staged 4..7, then 4..7")
+    ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl, rank_lo=0, rank_hi=4)
+    ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl, rank_lo=4, rank_hi=8)
     torch.cuda.synchronize()
-    ar.ar_set_packet_tuning(8, 0)       # small grids, so both launches are resident together
-    try:
-        announce("packet split launch: ranks 0..3 now, ranks 4..7 after 50 ms")
-        ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl_a, rank_lo=0, rank_hi=4, stream=s_a)
-        time.sleep(0.05)
-        ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl_b, rank_lo=4, rank_hi=8, stream=s_b)
-        torch.cuda.synchronize()
-    finally:
-        ar.ar_set_packet_tuning(0, 0)
-    assert ctrl_status(ctrl_a) == 0 and ctrl_status(ctrl_b) == 0
-    y = O.oneshot_sum(xs)
-    for t in outs:
-        assert np.array_equal(to_host(t), y)
+    assert ctrl_status(ctrl) == 0
+    for r in range(P):
+        assert np.array_equal(to_host(outs[r]), want[r])
+    got = _images(scratch)
+    for r in range(P):
+        assert np.array_equal(got[r], full[r])
+
+
+def _rank_mask(P, n, rank):
+    """Byte mask of the packets `rank` writes: its slot in every inbox and
+    every resbox."""
+    S = O.packet_slot_packets(P, n)
+    m = np.zeros((2 * P, 16 * S), bool)
+    m[rank] = True
+    m[P + rank] = True
+    return m.reshape(-1)
 
 
 @pytest.mark.parametrize("per_rank,wpl", [(1, 1), (3, 2), (7, 1), (0, 1), (0, 2), (64, 2)])
