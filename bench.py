@@ -78,6 +78,14 @@ class Row:
         self.step, self.note = step, note
 
 
+def packet_fused_bytes(P, n):
+    """Bytes one rank's share of the fused packet kernel must move: reads 2n
+    of input plus the P-1 foreign slots of its inbox and of its resbox (4 B
+    per element each; its own slots come from registers), writes 4n of
+    scatter packets, 4n of broadcast packets and 2n of output."""
+    return 2 * n + 2 * (4 * n * (P - 1) // P) + 10 * n
+
+
 def make_rows(names, torch, ar, I, W, stream):
     dev = torch.device("cuda:0")
 
@@ -113,8 +121,9 @@ def make_rows(names, torch, ar, I, W, stream):
             state["flag"] += 1  # every call carries the next flag
             ar.ar_packet_fused(ins, scratch, outs, state["flag"], ctrl, stream=stream)
 
-        row = Row(w.name, 20 * w.n * w.P, 1, packet_step,
-                  "graded launch: all 8 ranks; per rank 10n B read + 10n B written")
+        row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, packet_step,
+                  "graded launch: all 8 ranks; per rank 2n input + 4n(P-1)/P inbox + "
+                  "4n(P-1)/P resbox read (own slots come from registers), 10n written")
         row.ctrl = ctrl
         rows[w.name] = row
     if W.TWOSHOT_680x5120_R3.name in names:
@@ -152,7 +161,8 @@ def make_rows(names, torch, ar, I, W, stream):
             ar.ar_packet_recv(scratch, outs, st["flag"], ctrl, stream=stream)
 
         row = Row(w.name, 20 * w.n * w.P, 3, three_op,
-                  "send -> recv-reduce-send -> recv, one launch each; same bytes as fused")
+                  "send -> recv-reduce-send -> recv, one launch each; per rank 10n B read "
+                  "(own slots read back: separate launches) + 10n B written")
         row.ctrl = ctrl
         rows[w.name] = row
     if W.PACKET_EPOCH_GRAPH_512x7168.name in names:
@@ -172,7 +182,7 @@ def make_rows(names, torch, ar, I, W, stream):
         def replay(i, graph=graph):
             graph.replay()
 
-        row = Row(w.name, 20 * w.n * w.P, 1, replay,
+        row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, replay,
                   "fused kernel, flag = device epoch + 1, replayed from a HIP graph")
         row.ctrl = ctrl
         rows[w.name] = row
