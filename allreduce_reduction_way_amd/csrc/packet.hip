@@ -441,10 +441,18 @@ int packet_call(Kind kind, const ar_ptrs &in, const ar_ptrs &scratch, const ar_p
     FusedKernel fn = wpl == 1 ? pick_p<1>(P, kind) : pick_p<2>(P, kind);
 
     if (kind == kSend || kind == kRecvReduceSend || kind == kRecv) {
-        // Independent items, grid-stride; a modest grid leaves CUs free for a
-        // producer on another stream that a waiting phase depends on.
+        // Independent items, grid-stride.  The send phase never waits and
+        // takes a full grid; a waiting phase takes at most half of what is
+        // resident at once, leaving room for a producer that runs beside it.
         int64_t blocks = (int64_t)a.nranks * a.chunks;
-        if (blocks > (int64_t)dev.cus * 2) blocks = (int64_t)dev.cus * 2;
+        int64_t cap = (int64_t)dev.cus * 16;
+        if (kind != kSend) {
+            const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(fn));
+            if (per_cu <= 0) return AR_ELAUNCH;
+            cap = (int64_t)per_cu * dev.cus / 2;
+            if (cap < 1) cap = 1;
+        }
+        if (blocks > cap) blocks = cap;
         a.per_rank = 0;
         return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, kThreads, a, stream);
     }
