@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
             "ar_strerror": (ctypes.c_char_p, [i32]),
             "ar_noop": (i32, [vp]),
             "ar_set_reduce_tuning": (i32, [i32, i32, i32]),
-            "ar_set_packet_tuning": (i32, [i32, i32]),
+            "ar_set_packet_tuning": (i32, [i32, i32, i32]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -251,5 +251,5 @@ def ar_set_reduce_tuning(unroll: int = 0, threads: int = 0, max_blocks: int = 0)
     _check(lib().ar_set_reduce_tuning(unroll, threads, max_blocks), "ar_set_reduce_tuning")
 
 
-def ar_set_packet_tuning(per_rank: int = 0, words_per_lane: int = 0) -> None:
-    _check(lib().ar_set_packet_tuning(per_rank, words_per_lane), "ar_set_packet_tuning")
+def ar_set_packet_tuning(per_rank: int = 0, words_per_lane: int = 0, schedule: int = 0) -> None:
+    _check(lib().ar_set_packet_tuning(per_rank, words_per_lane, schedule), "ar_set_packet_tuning")

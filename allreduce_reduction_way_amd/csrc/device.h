@@ -74,14 +74,20 @@ __device__ __forceinline__ uint16_t reduce_elem(const uint16_t (&e)[P]) {
 
 // ---- plain 16-byte vector I/O ---------------------------------------------
 
+// NT: non-temporal (streaming) load.  Worth it only when the data cannot stay
+// in the 256 MB MALL anyway: measured on MI355X, the 4 x 64 Mi-element
+// two-shot (268 MB per launch) runs 178 us per four owners with it against
+// 190 us without, while the 72 MB write-mode share slows from 9.9 to 13.7 us.
+template <bool NT>
 __device__ __forceinline__ u32x4 load_vec(const void *base, int64_t elem) {
-    return *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem);
+    const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem);
+    if (NT) return __builtin_nontemporal_load(p);
+    return *p;
 }
 
 // Results are written once and never read back by the kernel, so they are
 // stored with the non-temporal (streaming) hint.  Measured on MI355X: 9.7 us
-// instead of 11.2 us for the 440x5120 x 8 write-mode share (non-temporal
-// loads, by contrast, were slower and are not used).
+// instead of 11.2 us for the 440x5120 x 8 write-mode share.
 __device__ __forceinline__ void store_vec(void *base, int64_t elem, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(base) + elem));
 }

@@ -321,6 +321,28 @@ __global__ __launch_bounds__(kThreads) void k_packet_phase(FusedArgs a) {
     }
 }
 
+// Role-split schedule of the fused kernel: the grid is three consecutive
+// ranges of R x B workgroups -- scatter, reduce-broadcast, receive -- and
+// workgroup (role, r, m) runs its phase for rank r over chunks m, m + B, ...
+// A role only waits on roles before it (reduce on scatter, receive on reduce),
+// scatter never waits, and producers come first in workgroup order; with the
+// whole grid resident every wait is satisfied.  The own slots are read back
+// (no register carry across roles).
+template <int P, int WPL>
+__global__ __launch_bounds__(kThreads) void k_packet_roles(FusedArgs a) {
+    const int64_t per_role = (int64_t)a.nranks * a.per_rank;
+    const int role = (int)(blockIdx.x / per_role);
+    const int64_t b = blockIdx.x % per_role;
+    const int r = a.rank_lo + (int)(b % a.nranks);
+    const int64_t m = b / a.nranks;
+    uint32_t unused_d[WPL], unused_res[WPL];
+    for (int64_t c = m; c < a.chunks; c += a.per_rank) {
+        if (!pipeline_step<P, WPL, false>(a, a.flag, r, role == 0, c, role == 1, c, role == 2, c,
+                                          unused_d, unused_res))
+            return;
+    }
+}
+
 typedef void (*FusedKernel)(FusedArgs);
 
 template <int P, int WPL>
@@ -330,7 +352,8 @@ FusedKernel pick_kind(int kind) {
         case 1: return k_packet_fused<P, WPL, true>;
         case 2: return k_packet_phase<P, WPL, 0>;
         case 3: return k_packet_phase<P, WPL, 1>;
-        default: return k_packet_phase<P, WPL, 2>;
+        case 4: return k_packet_phase<P, WPL, 2>;
+        default: return k_packet_roles<P, WPL>;
     }
 }
 
@@ -347,12 +370,13 @@ FusedKernel pick_p(int P, int kind) {
     }
 }
 
-enum Kind { kFused = 0, kFusedEpoch = 1, kSend = 2, kRecvReduceSend = 3, kRecv = 4 };
+enum Kind { kFused = 0, kFusedEpoch = 1, kSend = 2, kRecvReduceSend = 3, kRecv = 4, kRoles = 5 };
 
 // Launch-shape overrides for benchmark sweeps: workgroups per rank and words
 // per lane per chunk (0 = automatic).
 int g_fused_per_rank_override = 0;
 int g_fused_wpl_override = 0;
+int g_fused_schedule = 0;  // 0 pipelined workgroups, 1 role-split workgroups
 
 // Validates one packet-path call and fills the kernel arguments.  `use_in`,
 // `use_out`, `use_ctrl` say which buffers the entry point touches; every
@@ -422,11 +446,13 @@ int prepare_packet(const ar_ptrs &in, const ar_ptrs &scratch, const ar_ptrs &out
     return AR_OK;
 }
 
-int packet_call(Kind kind, const ar_ptrs &in, const ar_ptrs &scratch, const ar_ptrs &out, int P,
+int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const ar_ptrs &out, int P,
                 int rank_lo, int rank_hi, int64_t n, uint32_t flag, void *ctrl, uint64_t max_spins,
                 void *stream) {
-    const bool use_in = kind == kFused || kind == kFusedEpoch || kind == kSend;
-    const bool use_out = kind == kFused || kind == kFusedEpoch || kind == kRecv;
+    Kind kind = kind_in;
+    if (kind == kFused && g_fused_schedule == 1) kind = kRoles;
+    const bool use_in = kind == kFused || kind == kFusedEpoch || kind == kSend || kind == kRoles;
+    const bool use_out = kind == kFused || kind == kFusedEpoch || kind == kRecv || kind == kRoles;
     const bool use_ctrl = kind != kSend;
     // Two words per lane per chunk: 120.8 us against 125.1 us with one word
     // for 512x7168 x 8 on MI355X (fewer, wider chunks; 134 VGPRs, 3
@@ -463,7 +489,8 @@ int packet_call(Kind kind, const ar_ptrs &in, const ar_ptrs &scratch, const ar_p
     const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(fn));
     if (per_cu <= 0) return AR_ELAUNCH;
     const int64_t resident = (int64_t)per_cu * dev.cus;
-    int64_t B = resident / a.nranks;
+    const int64_t roles = kind == kRoles ? 3 : 1;
+    int64_t B = resident / (a.nranks * roles);
     if (g_fused_per_rank_override > 0 && g_fused_per_rank_override < B)
         B = g_fused_per_rank_override;
     if (B > a.chunks) B = a.chunks;
@@ -471,8 +498,8 @@ int packet_call(Kind kind, const ar_ptrs &in, const ar_ptrs &scratch, const ar_p
     const int64_t rounds = (a.chunks + B - 1) / B;
     B = (a.chunks + rounds - 1) / rounds;
     a.per_rank = (int)B;
-    return launch(reinterpret_cast<const void *>(fn), (unsigned)(B * a.nranks), kThreads, a,
-                  stream);
+    return launch(reinterpret_cast<const void *>(fn), (unsigned)(roles * B * a.nranks), kThreads,
+                  a, stream);
 }
 
 }  // namespace
@@ -563,11 +590,13 @@ int ar_packet_recv(ar_ptrs scratch, ar_ptrs out, int P, int rank_lo, int rank_hi
 
 // Benchmark-only override of the packet kernels' workgroups per rank (0 =
 // auto; never above the resident limit) and words per lane per chunk.
-int ar_set_packet_tuning(int per_rank, int words_per_lane) {
-    if (per_rank < 0 || !(words_per_lane == 0 || words_per_lane == 1 || words_per_lane == 2))
+int ar_set_packet_tuning(int per_rank, int words_per_lane, int schedule) {
+    if (per_rank < 0 || !(words_per_lane == 0 || words_per_lane == 1 || words_per_lane == 2) ||
+        !(schedule == 0 || schedule == 1))
         return AR_EINVAL;
     g_fused_per_rank_override = per_rank;
     g_fused_wpl_override = words_per_lane;
+    g_fused_schedule = schedule;
     return AR_OK;
 }
 

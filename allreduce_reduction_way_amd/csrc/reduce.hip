@@ -32,7 +32,7 @@ struct ReduceArgs {
     int64_t ntail;  // scalar elements after the bulk
 };
 
-template <int P, bool BCAST, int U>
+template <int P, bool BCAST, int U, bool NTL>
 __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
     constexpr int NOUT = BCAST ? P : 1;
     const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
             const int64_t v = v0 + u * nthreads;
             if (v < a.nvec) {
 #pragma unroll
-                for (int p = 0; p < P; ++p) x[u][p] = load_vec(a.in.p[p], a.head + 8 * v);
+                for (int p = 0; p < P; ++p) x[u][p] = load_vec<NTL>(a.in.p[p], a.head + 8 * v);
             }
         }
 #pragma unroll
@@ -76,27 +76,36 @@ __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
 
 typedef void (*ReduceKernel)(ReduceArgs);
 
-template <int P, bool BCAST>
+template <int P, bool BCAST, bool NTL>
 ReduceKernel pick_unroll(int U) {
     switch (U) {
-        case 1: return k_reduce<P, BCAST, 1>;
-        case 2: return k_reduce<P, BCAST, 2>;
-        default: return k_reduce<P, BCAST, 4>;
+        case 1: return k_reduce<P, BCAST, 1, NTL>;
+        case 2: return k_reduce<P, BCAST, 2, NTL>;
+        default: return k_reduce<P, BCAST, 4, NTL>;
     }
 }
 
-template <bool BCAST>
-ReduceKernel pick(int P, int U) {
+template <bool BCAST, bool NTL>
+ReduceKernel pick_p(int P, int U) {
     switch (P) {
-        case 2: return pick_unroll<2, BCAST>(U);
-        case 3: return pick_unroll<3, BCAST>(U);
-        case 4: return pick_unroll<4, BCAST>(U);
-        case 5: return pick_unroll<5, BCAST>(U);
-        case 6: return pick_unroll<6, BCAST>(U);
-        case 7: return pick_unroll<7, BCAST>(U);
-        default: return pick_unroll<8, BCAST>(U);
+        case 2: return pick_unroll<2, BCAST, NTL>(U);
+        case 3: return pick_unroll<3, BCAST, NTL>(U);
+        case 4: return pick_unroll<4, BCAST, NTL>(U);
+        case 5: return pick_unroll<5, BCAST, NTL>(U);
+        case 6: return pick_unroll<6, BCAST, NTL>(U);
+        case 7: return pick_unroll<7, BCAST, NTL>(U);
+        default: return pick_unroll<8, BCAST, NTL>(U);
     }
 }
+
+ReduceKernel pick(bool bcast, bool ntl, int P, int U) {
+    if (bcast) return ntl ? pick_p<true, true>(P, U) : pick_p<true, false>(P, U);
+    return ntl ? pick_p<false, true>(P, U) : pick_p<false, false>(P, U);
+}
+
+// Bytes one launch touches beyond which its inputs take non-temporal loads:
+// half the 256 MB MALL, so data that could stay cached keeps plain loads.
+constexpr int64_t kStreamingBytes = 128ll << 20;
 
 // Launch shape overrides for benchmark sweeps (0 = automatic).
 int g_unroll_override = 0;
@@ -171,7 +180,8 @@ int launch_reduce(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast
     if (scalar_blocks > blocks) blocks = scalar_blocks;
     if (blocks > (int64_t)dev.cus * 16) blocks = (int64_t)dev.cus * 16;  // lanes loop beyond
     if (blocks < 1) blocks = 1;
-    ReduceKernel fn = bcast ? pick<true>(P, U) : pick<false>(P, U);
+    const int64_t touched = (int64_t)(P + (bcast ? P : 1)) * len * 2;
+    ReduceKernel fn = pick(bcast, touched > kStreamingBytes, P, U);
     return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, (unsigned)threads, a, stream);
 }
 

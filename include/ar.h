@@ -266,10 +266,12 @@ int ar_noop(void *stream);
  * workgroups (0 = automatic) for ar_oneshot_sum, ar_oneshot_write_bcast and
  * ar_twoshot_share.  ar_set_packet_tuning: workgroups per emulated rank of
  * ar_packet_fused (0 = automatic; never more than fit on the device at once)
- * and words per lane per chunk in {0 = automatic, 1, 2}.  Results do not
- * depend on either. */
+ * words per lane per chunk in {0 = automatic, 1, 2}, and the schedule of
+ * ar_packet_fused: 0 = every workgroup runs all phases of its chunks as a
+ * pipeline, 1 = separate scatter, reduce-broadcast and receive workgroups in
+ * one grid.  Results do not depend on any of them. */
 int ar_set_reduce_tuning(int unroll, int threads, int max_blocks);
-int ar_set_packet_tuning(int per_rank, int words_per_lane);
+int ar_set_packet_tuning(int per_rank, int words_per_lane, int schedule);
 
 #ifdef __cplusplus
 }

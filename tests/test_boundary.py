@@ -183,10 +183,11 @@ def test_tuning_validation():
     assert _err(ar.ar_set_reduce_tuning, 3, 0, 0) == ar.AR_EINVAL
     assert _err(ar.ar_set_reduce_tuning, 1, 0, -1) == ar.AR_EINVAL
     assert _err(ar.ar_set_reduce_tuning, 1, 96, 0) == ar.AR_EINVAL
-    assert _err(ar.ar_set_packet_tuning, -1, 0) == ar.AR_EINVAL
-    assert _err(ar.ar_set_packet_tuning, 0, 3) == ar.AR_EINVAL
+    assert _err(ar.ar_set_packet_tuning, -1, 0, 0) == ar.AR_EINVAL
+    assert _err(ar.ar_set_packet_tuning, 0, 3, 0) == ar.AR_EINVAL
+    assert _err(ar.ar_set_packet_tuning, 0, 0, 2) == ar.AR_EINVAL
     ar.ar_set_reduce_tuning(0, 0, 0)
-    ar.ar_set_packet_tuning(0, 0)
+    ar.ar_set_packet_tuning(0, 0, 0)
 
 
 def test_reduce_scatter_validation():

@@ -246,23 +246,25 @@ def _rank_mask(P, n, rank):
     return m.reshape(-1)
 
 
+@pytest.mark.parametrize("schedule", [0, 1])
 @pytest.mark.parametrize("per_rank,wpl", [(1, 1), (3, 2), (7, 1), (0, 1), (0, 2), (64, 2)])
 @pytest.mark.parametrize("P,n", [(8, 8192 * 9 + 1), (3, 4096 * 7 + 5)])
-def test_packet_fused_every_launch_shape(per_rank, wpl, P, n):
+def test_packet_fused_every_launch_shape(per_rank, wpl, P, n, schedule):
     """Pipeline depth (chunks per workgroup) and chunk width change the
     schedule, never the result: outputs and scratch images stay bit-exact."""
     xs = I.make_inputs("uniform", P, n, seed=per_rank + wpl)
     scratch = _scratch(P, n)
     outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
     ctrl = ctrl_block()
-    ar.ar_set_packet_tuning(per_rank, wpl)
+    ar.ar_set_packet_tuning(per_rank, wpl, schedule)
     try:
-        announce(f"packet launch shape per_rank={per_rank} wpl={wpl} P={P} n={n}")
+        announce(f"packet launch shape per_rank={per_rank} wpl={wpl} schedule={schedule} "
+                 f"P={P} n={n}")
         for f in (1, 2):
             ar.ar_packet_fused([to_dev(x) for x in xs], scratch, outs, f, ctrl)
         torch.cuda.synchronize()
     finally:
-        ar.ar_set_packet_tuning(0, 0)
+        ar.ar_set_packet_tuning(0, 0, 0)
     assert ctrl_status(ctrl) == 0
     zero = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
     _, img1 = O.packet_fused(xs, 1, zero)

@@ -214,3 +214,23 @@ def test_twoshot_64Mi_p4_all_owners_workload():
     y = O.oneshot_sum(xs)
     for t in d_out:
         assert np.array_equal(to_host(t), y)
+
+
+@pytest.mark.parametrize("P,n,op", [(8, (8 << 20) + 13, "oneshot"), (3, (24 << 20) + 5, "bcast")])
+def test_streaming_size_takes_nontemporal_loads_and_matches(P, n, op):
+    """Calls touching more than 128 MiB take non-temporal loads: same results."""
+    xs = I.make_inputs("uniform", P, n, seed=P)
+    d_in = [to_dev(x) for x in xs]
+    announce(f"streaming-size {op} P={P} n={n}")
+    y = O.oneshot_sum(xs)
+    if op == "oneshot":
+        out = torch.empty(n, dtype=torch.int16, device="cuda:0")
+        ar.ar_oneshot_sum(d_in, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(out), y)
+    else:
+        outs = [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(P)]
+        ar.ar_oneshot_write_bcast(d_in, outs)
+        torch.cuda.synchronize()
+        for t in outs:
+            assert np.array_equal(to_host(t), y)
