@@ -43,6 +43,14 @@ PACKET_EPOCH_GRAPH_512x7168 = Workload("packet_epoch_graph_512x7168_p8", "packet
 REDUCE_SCATTER_440x5120_R3 = Workload("reduce_scatter_440x5120_p8_rank3", "reduce_scatter", 8,
                                       440 * 5120, "uniform", ranks=(3,))
 
+# One rank's share of the packet path on its own: rank 3 of 8 against peer
+# packets already in place; and the LL codec alone on one rank's 512x7168.
+PACKET_RANK3_512x7168 = Workload("packet_rank3_share_512x7168_p8", "packet_rank", 8, 512 * 7168,
+                                 "uniform", ranks=(3,))
+LL_ENCODE_512x7168 = Workload("ll_encode_512x7168", "ll_encode", 1, 512 * 7168, "uniform")
+LL_DECODE_512x7168 = Workload("ll_decode_512x7168", "ll_decode", 1, 512 * 7168, "uniform")
+
 ALL = (ONESHOT_4K, WRITE_BCAST_440x5120, PACKET_512x7168, TWOSHOT_680x5120_R3, TWOSHOT_64Mi_P4,
-       PACKET_3OP_512x7168, PACKET_EPOCH_GRAPH_512x7168, REDUCE_SCATTER_440x5120_R3)
+       PACKET_3OP_512x7168, PACKET_EPOCH_GRAPH_512x7168, REDUCE_SCATTER_440x5120_R3,
+       PACKET_RANK3_512x7168, LL_ENCODE_512x7168, LL_DECODE_512x7168)
 BY_NAME = {w.name: w for w in ALL}

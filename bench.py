@@ -195,6 +195,43 @@ def make_rows(names, torch, ar, I, W, stream):
                            lambda i, ins=ins, out=out, rc=rc: ar.ar_reduce_scatter_share(
                                ins, out, 3, rc, stream=stream),
                            "rank 3's block: read P x block, write 1 x block")
+    if W.PACKET_RANK3_512x7168.name in names:
+        w = W.PACKET_RANK3_512x7168
+        ins = dev_inputs(w)
+        nb = ar.ar_packet_scratch_bytes(w.P, w.n)
+        scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
+        outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
+        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        # stage every rank's packets for flag 1 with one full call; rank 3
+        # then re-runs its share against them (rewriting its own packets with
+        # the same values) on every step
+        ar.ar_packet_fused(ins, scratch, outs, 1, ctrl, stream=stream)
+        torch.cuda.synchronize()
+        row = Row(w.name, packet_fused_bytes(w.P, w.n), 1,
+                  lambda i, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl: ar.ar_packet_fused(
+                      ins, scratch, outs, 1, ctrl, rank_lo=3, rank_hi=4, stream=stream),
+                  "rank 3 alone, peers' packets staged: one rank's share of the packet path")
+        row.ctrl = ctrl
+        rows[w.name] = row
+    if W.LL_ENCODE_512x7168.name in names or W.LL_DECODE_512x7168.name in names:
+        w = W.LL_ENCODE_512x7168
+        src = dev_inputs(w)[0]
+        pk = torch.zeros(16 * ar.ar_ll_packets(w.n), dtype=torch.uint8, device=dev)
+        dst = torch.empty(w.n, dtype=torch.int16, device=dev)
+        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        ar.ar_ll_encode(src, pk, 1, stream=stream)
+        torch.cuda.synchronize()
+        if w.name in names:
+            rows[w.name] = Row(w.name, 6 * w.n, 1,
+                               lambda i, src=src, pk=pk: ar.ar_ll_encode(src, pk, 1, stream=stream),
+                               "read 2 B, write 4 B per element")
+        if W.LL_DECODE_512x7168.name in names:
+            row = Row(W.LL_DECODE_512x7168.name, 6 * w.n, 1,
+                      lambda i, pk=pk, dst=dst, ctrl=ctrl: ar.ar_ll_decode(pk, dst, 1, ctrl,
+                                                                           stream=stream),
+                      "read 4 B (flags already in place), write 2 B per element")
+            row.ctrl = ctrl
+            rows[W.LL_DECODE_512x7168.name] = row
     return rows
 
 
