@@ -71,11 +71,16 @@ def log(msg: str) -> None:
 # ----------------------------------------------------------------------- setup
 
 class Row:
-    """One workload: device buffers plus a `step(i)` that launches one step."""
+    """One workload: device buffers plus `factory(stream_handle)`, which
+    returns `step(i)` launching one step on that stream through the C ABI
+    with its arguments marshalled once, up front (what a C or C++ caller
+    pays per call).  `graphable` rows have no per-call state and are also
+    timed as a captured HIP graph of back-to-back calls."""
 
-    def __init__(self, name, alg_bytes, launches_per_step, step, note):
+    def __init__(self, name, alg_bytes, launches_per_step, factory, note, graphable=False):
         self.name, self.alg_bytes, self.launches = name, alg_bytes, launches_per_step
-        self.step, self.note = step, note
+        self.factory, self.note, self.graphable = factory, note, graphable
+        self.step = None
 
 
 def packet_fused_bytes(P, n):
@@ -86,42 +91,69 @@ def packet_fused_bytes(P, n):
     return 2 * n + 2 * (4 * n * (P - 1) // P) + 10 * n
 
 
-def make_rows(names, torch, ar, I, W, stream):
+def _raw(ar, name, *args):
+    """A call of C entry point `name` with pre-marshalled arguments; checked
+    once here, then returned for the timed loops."""
+    fn = getattr(ar.lib(), name)
+    rc = fn(*args)
+    if rc != 0:
+        raise ar.ArError(rc, name)
+    return lambda: fn(*args)
+
+
+def make_rows(names, torch, ar, I, W):
     dev = torch.device("cuda:0")
+    P_ = ar._ptrs
 
     def dev_inputs(w, seed=0):
         import numpy as np
         return [torch.from_numpy(x.view(np.int16)).to(dev) for x in I.make_inputs(w.dist, w.P, w.n, seed)]
+
+    def ctrl_block():
+        return torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
 
     rows = {}
     if W.WRITE_BCAST_440x5120.name in names:
         w = W.WRITE_BCAST_440x5120
         ins = dev_inputs(w)
         outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
-        rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, 1,
-                           lambda i, ins=ins, outs=outs: ar.ar_oneshot_write_bcast(ins, outs, stream=stream),
-                           "read P inputs + write P outputs")
+
+        def f(s, ins=ins, outs=outs, w=w):
+            c = _raw(ar, "ar_oneshot_write_bcast", P_(ins), P_(outs), w.P, w.n, s)
+            return lambda i: c()
+
+        rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, 1, f, "read P inputs + write P outputs",
+                           graphable=True)
     if W.ONESHOT_4K.name in names:
         w = W.ONESHOT_4K
         ins = dev_inputs(w)
         out = torch.empty(w.n, dtype=torch.int16, device=dev)
-        rows[w.name] = Row(w.name, (w.P + 1) * w.n * 2, 1,
-                           lambda i, ins=ins, out=out: ar.ar_oneshot_sum(ins, out, stream=stream),
-                           "latency-bound: compare with the empty-kernel floor")
+
+        def f(s, ins=ins, out=out, w=w):
+            c = _raw(ar, "ar_oneshot_sum", P_(ins), out.data_ptr(), w.P, w.n, s)
+            return lambda i: c()
+
+        rows[w.name] = Row(w.name, (w.P + 1) * w.n * 2, 1, f,
+                           "latency-bound: compare with the empty-kernel floor", graphable=True)
     if W.PACKET_512x7168.name in names:
         w = W.PACKET_512x7168
         ins = dev_inputs(w)
         nb = ar.ar_packet_scratch_bytes(w.P, w.n)
         scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
         outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
-        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        ctrl = ctrl_block()
         state = {"flag": 0}
 
-        def packet_step(i, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl, state=state):
-            state["flag"] += 1  # every call carries the next flag
-            ar.ar_packet_fused(ins, scratch, outs, state["flag"], ctrl, stream=stream)
+        def f(s, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl, st=state, w=w):
+            fn = ar.lib().ar_packet_fused
+            a = (P_(ins), P_(scratch), P_(outs), w.P, 0, w.P, w.n)
 
-        row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, packet_step,
+            def step(i):
+                st["flag"] += 1  # every call carries the next flag
+                fn(*a, st["flag"], ctrl.data_ptr(), 0, s)
+            return step
+
+        row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, f,
                   "graded launch: all 8 ranks; per rank 2n input + 4n(P-1)/P inbox + "
                   "4n(P-1)/P resbox read (own slots come from registers), 10n written")
         row.ctrl = ctrl
@@ -131,36 +163,49 @@ def make_rows(names, torch, ar, I, W, stream):
         ins = dev_inputs(w)
         outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
         b, e = ar.ar_slice_range(w.P, 3, w.n)
-        rows[w.name] = Row(w.name, 2 * w.P * (e - b) * 2, 1,
-                           lambda i, ins=ins, outs=outs: ar.ar_twoshot_share(ins, outs, 3, stream=stream),
-                           "rank 3's slice: read P x slice, write P x slice")
+
+        def f(s, ins=ins, outs=outs, w=w):
+            c = _raw(ar, "ar_twoshot_share", P_(ins), P_(outs), w.P, 3, w.n, s)
+            return lambda i: c()
+
+        rows[w.name] = Row(w.name, 2 * w.P * (e - b) * 2, 1, f,
+                           "rank 3's slice: read P x slice, write P x slice", graphable=True)
     if W.TWOSHOT_64Mi_P4.name in names:
         w = W.TWOSHOT_64Mi_P4
         ins = dev_inputs(w)
         outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
 
-        def owners(i, ins=ins, outs=outs, w=w):
-            for r in w.ranks:
-                ar.ar_twoshot_share(ins, outs, r, stream=stream)
+        def f(s, ins=ins, outs=outs, w=w):
+            cs = [_raw(ar, "ar_twoshot_share", P_(ins), P_(outs), w.P, r, w.n, s) for r in w.ranks]
 
-        rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, len(w.ranks), owners,
-                           "4 owner launches per step, full buffer into 4 outputs")
+            def step(i):
+                for c in cs:
+                    c()
+            return step
+
+        rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, len(w.ranks), f,
+                           "4 owner launches per step, full buffer into 4 outputs", graphable=True)
     if W.PACKET_3OP_512x7168.name in names:
         w = W.PACKET_3OP_512x7168
         ins = dev_inputs(w)
         nb = ar.ar_packet_scratch_bytes(w.P, w.n)
         scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
         outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
-        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        ctrl = ctrl_block()
         state3 = {"flag": 0}
 
-        def three_op(i, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl, st=state3, n=w.n):
-            st["flag"] += 1
-            ar.ar_packet_send(ins, scratch, st["flag"], stream=stream)
-            ar.ar_packet_recv_reduce_send(scratch, n, st["flag"], ctrl, stream=stream)
-            ar.ar_packet_recv(scratch, outs, st["flag"], ctrl, stream=stream)
+        def f(s, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl, st=state3, w=w):
+            L = ar.lib()
+            pi, ps, po, c = P_(ins), P_(scratch), P_(outs), ctrl.data_ptr()
 
-        row = Row(w.name, 20 * w.n * w.P, 3, three_op,
+            def step(i):
+                st["flag"] += 1
+                L.ar_packet_send(pi, ps, w.P, 0, w.P, w.n, st["flag"], s)
+                L.ar_packet_recv_reduce_send(ps, w.P, 0, w.P, w.n, st["flag"], c, 0, s)
+                L.ar_packet_recv(ps, po, w.P, 0, w.P, w.n, st["flag"], c, 0, s)
+            return step
+
+        row = Row(w.name, 20 * w.n * w.P, 3, f,
                   "send -> recv-reduce-send -> recv, one launch each; per rank 10n B read "
                   "(own slots read back: separate launches) + 10n B written")
         row.ctrl = ctrl
@@ -171,18 +216,18 @@ def make_rows(names, torch, ar, I, W, stream):
         nb = ar.ar_packet_scratch_bytes(w.P, w.n)
         scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
         outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
-        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
-        ar.ar_packet_fused_epoch(ins, scratch, outs, ctrl, stream=stream)  # warm-up, flag 1
+        ctrl = ctrl_block()
+        ar.ar_packet_fused_epoch(ins, scratch, outs, ctrl)  # warm-up, flag 1
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             ar.ar_packet_fused_epoch(ins, scratch, outs, ctrl)
         torch.cuda.synchronize()
 
-        def replay(i, graph=graph):
-            graph.replay()
+        def f(s, graph=graph):
+            return lambda i: graph.replay()  # replays on the current stream
 
-        row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, replay,
+        row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, f,
                   "fused kernel, flag = device epoch + 1, replayed from a HIP graph")
         row.ctrl = ctrl
         rows[w.name] = row
@@ -191,26 +236,34 @@ def make_rows(names, torch, ar, I, W, stream):
         ins = dev_inputs(w)
         rc = w.n // w.P
         out = torch.empty(rc, dtype=torch.int16, device=dev)
-        rows[w.name] = Row(w.name, (w.P + 1) * rc * 2, 1,
-                           lambda i, ins=ins, out=out, rc=rc: ar.ar_reduce_scatter_share(
-                               ins, out, 3, rc, stream=stream),
-                           "rank 3's block: read P x block, write 1 x block")
+
+        def f(s, ins=ins, out=out, w=w, rc=rc):
+            c = _raw(ar, "ar_reduce_scatter_share", P_(ins), out.data_ptr(), w.P, 3, rc, s)
+            return lambda i: c()
+
+        rows[w.name] = Row(w.name, (w.P + 1) * rc * 2, 1, f,
+                           "rank 3's block: read P x block, write 1 x block", graphable=True)
     if W.PACKET_RANK3_512x7168.name in names:
         w = W.PACKET_RANK3_512x7168
         ins = dev_inputs(w)
         nb = ar.ar_packet_scratch_bytes(w.P, w.n)
         scratch = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(w.P)]
         outs = [torch.empty(w.n, dtype=torch.int16, device=dev) for _ in range(w.P)]
-        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
+        ctrl = ctrl_block()
         # stage every rank's packets for flag 1 with one full call; rank 3
         # then re-runs its share against them (rewriting its own packets with
         # the same values) on every step
-        ar.ar_packet_fused(ins, scratch, outs, 1, ctrl, stream=stream)
+        ar.ar_packet_fused(ins, scratch, outs, 1, ctrl)
         torch.cuda.synchronize()
-        row = Row(w.name, packet_fused_bytes(w.P, w.n), 1,
-                  lambda i, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl: ar.ar_packet_fused(
-                      ins, scratch, outs, 1, ctrl, rank_lo=3, rank_hi=4, stream=stream),
-                  "rank 3 alone, peers' packets staged: one rank's share of the packet path")
+
+        def f(s, ins=ins, scratch=scratch, outs=outs, ctrl=ctrl, w=w):
+            c = _raw(ar, "ar_packet_fused", P_(ins), P_(scratch), P_(outs), w.P, 3, 4, w.n, 1,
+                     ctrl.data_ptr(), 0, s)
+            return lambda i: c()
+
+        row = Row(w.name, packet_fused_bytes(w.P, w.n), 1, f,
+                  "rank 3 alone, peers' packets staged: one rank's share of the packet path",
+                  graphable=True)
         row.ctrl = ctrl
         rows[w.name] = row
     if W.LL_ENCODE_512x7168.name in names or W.LL_DECODE_512x7168.name in names:
@@ -218,18 +271,24 @@ def make_rows(names, torch, ar, I, W, stream):
         src = dev_inputs(w)[0]
         pk = torch.zeros(16 * ar.ar_ll_packets(w.n), dtype=torch.uint8, device=dev)
         dst = torch.empty(w.n, dtype=torch.int16, device=dev)
-        ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
-        ar.ar_ll_encode(src, pk, 1, stream=stream)
+        ctrl = ctrl_block()
+        ar.ar_ll_encode(src, pk, 1)
         torch.cuda.synchronize()
         if w.name in names:
-            rows[w.name] = Row(w.name, 6 * w.n, 1,
-                               lambda i, src=src, pk=pk: ar.ar_ll_encode(src, pk, 1, stream=stream),
-                               "read 2 B, write 4 B per element")
+            def f(s, src=src, pk=pk, w=w):
+                c = _raw(ar, "ar_ll_encode", src.data_ptr(), pk.data_ptr(), w.n, 1, s)
+                return lambda i: c()
+
+            rows[w.name] = Row(w.name, 6 * w.n, 1, f, "read 2 B, write 4 B per element",
+                               graphable=True)
         if W.LL_DECODE_512x7168.name in names:
-            row = Row(W.LL_DECODE_512x7168.name, 6 * w.n, 1,
-                      lambda i, pk=pk, dst=dst, ctrl=ctrl: ar.ar_ll_decode(pk, dst, 1, ctrl,
-                                                                           stream=stream),
-                      "read 4 B (flags already in place), write 2 B per element")
+            def f(s, pk=pk, dst=dst, ctrl=ctrl, w=w):
+                c = _raw(ar, "ar_ll_decode", pk.data_ptr(), dst.data_ptr(), w.n, 1,
+                         ctrl.data_ptr(), 0, s)
+                return lambda i: c()
+
+            row = Row(W.LL_DECODE_512x7168.name, 6 * w.n, 1, f,
+                      "read 4 B (flags already in place), write 2 B per element", graphable=True)
             row.ctrl = ctrl
             rows[W.LL_DECODE_512x7168.name] = row
     return rows
@@ -271,6 +330,30 @@ def time_per_call(torch, stream, fn, calls, scrub=None):
     ms = sorted(a.elapsed_time(b) for a, b in evs)
     return {"mean_us": 1e3 * sum(ms) / len(ms), "median_us": 1e3 * ms[len(ms) // 2],
             "best_us": 1e3 * ms[0], "worst_us": 1e3 * ms[-1]}
+
+
+def time_graph(torch, stream, row, calls=100, replays=20):
+    """Per-call time of `calls` back-to-back calls captured in one HIP graph:
+    the device-side cost with no host launch work in between."""
+    g = torch.cuda.CUDAGraph()
+    capture = torch.cuda.Stream()
+    step = row.factory(int(capture.cuda_stream))   # marshalled (and checked once) eagerly
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=capture):
+        for i in range(calls):
+            step(i)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / (replays * calls)
 
 
 def gbs(nbytes, us):
@@ -353,7 +436,9 @@ def main():
     if args.rows:
         names = sorted(set([headline.name] + args.rows.split(",")))
     log("allocating and filling inputs")
-    rows = make_rows(names, torch, ar, I, W, int(stream.cuda_stream))
+    rows = make_rows(names, torch, ar, I, W)
+    for row in rows.values():
+        row.step = row.factory(int(stream.cuda_stream))
 
     # headline: streamed timed region
     h = rows[headline.name]
@@ -405,7 +490,10 @@ def main():
             cold = time_per_call(torch, stream, row.step, args.cold_calls, scrub=scrub)
             del scrub
             us = ms_r * 1e3
+            graph_us = time_graph(torch, stream, row) if row.graphable else None
             out_rows[name] = {
+                "graph_us_per_call": round(graph_us, 3) if graph_us else None,
+                "graph_gbs": round(gbs(row.alg_bytes, graph_us), 1) if graph_us else None,
                 "streamed_us_per_call": round(us, 3),
                 "streamed_gbs": round(gbs(row.alg_bytes, us), 1),
                 "per_call_us": {k: round(v, 3) for k, v in pc.items()},
@@ -422,10 +510,14 @@ def main():
                 torch.cuda.synchronize()
                 out_rows[name]["device_status"] = int(row.ctrl.view(torch.int32)[0].item())
         log("empty-kernel floor")
-        floor_ms, _ = time_streamed(torch, stream, lambda i: ar.ar_noop(stream=int(stream.cuda_stream)),
-                                    2000, 50)
-        floor_pc = time_per_call(torch, stream, lambda i: ar.ar_noop(stream=int(stream.cuda_stream)), 200)
-        out_rows["empty_kernel_floor"] = {"streamed_us_per_call": round(floor_ms * 1e3, 3),
+        noop = Row("empty_kernel_floor", 0, 1,
+                   lambda s_: (lambda c: (lambda i: c()))(_raw(ar, "ar_noop", s_)),
+                   "empty kernel", graphable=True)
+        noop.step = noop.factory(int(stream.cuda_stream))
+        floor_ms, _ = time_streamed(torch, stream, noop.step, 2000, 50)
+        floor_pc = time_per_call(torch, stream, noop.step, 200)
+        out_rows["empty_kernel_floor"] = {"graph_us_per_call": round(time_graph(torch, stream, noop), 3),
+                                          "streamed_us_per_call": round(floor_ms * 1e3, 3),
                                           "per_call_us": {k: round(v, 3) for k, v in floor_pc.items()}}
         result["rows"] = out_rows
 
