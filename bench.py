@@ -81,6 +81,9 @@ class Row:
         self.name, self.alg_bytes, self.launches = name, alg_bytes, launches_per_step
         self.factory, self.note, self.graphable = factory, note, graphable
         self.step = None
+        # The device buffers a row's launches (and captured graphs) address:
+        # bound here too, so they live exactly as long as the row.
+        self.keep = tuple(v for v in (factory.__defaults__ or ()) if v is not None)
 
 
 def packet_fused_bytes(P, n):
@@ -224,7 +227,10 @@ def make_rows(names, torch, ar, I, W):
             ar.ar_packet_fused_epoch(ins, scratch, outs, ctrl)
         torch.cuda.synchronize()
 
-        def f(s, graph=graph):
+        # the graph holds raw addresses: the factory must keep every buffer it
+        # captured alive (torch.cuda.graph() empties torch's cache on entry, so
+        # a dropped tensor here would be unmapped under the graph)
+        def f(s, graph=graph, keep=(ins, scratch, outs, ctrl)):
             return lambda i: graph.replay()  # replays on the current stream
 
         row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, f,
