@@ -373,7 +373,7 @@ def traffic_from_profiles(headline: str, launches_alg_bytes: int):
     if not path.exists():
         return None
     text = path.read_text()
-    m = re.search(r"kernel source hash:\s*`?([0-9a-f]{16})", text)
+    m = re.search(r"[Kk]ernel source hash[^`]*`([0-9a-f]{16})`", text)
     if not m or m.group(1) != kernel_source_hash():
         return None
     m = re.search(r"scaled HBM bytes per launch:\s*([0-9.]+)", text)

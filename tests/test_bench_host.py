@@ -1,0 +1,48 @@
+"""CPU checks of bench.py's host logic: the counter summaries it reads parse,
+and the byte accounting of the packet share matches its definition."""
+from __future__ import annotations
+
+import pathlib
+import re
+
+import bench
+
+PROFILES = pathlib.Path(__file__).resolve().parents[1] / "profiles"
+
+
+def test_counter_summaries_parse():
+    for name in ("write_bcast_440x5120_p8_counters.md", "packet_fused_512x7168_p8_counters.md"):
+        text = (PROFILES / name).read_text()
+        assert re.search(r"[Kk]ernel source hash[^`]*`([0-9a-f]{16})`", text), name
+        m = re.search(r"scaled HBM bytes per launch:\s*([0-9.]+)", text)
+        assert m and float(m.group(1)) > 0, name
+
+
+def test_traffic_is_reported_only_for_the_profiled_sources(monkeypatch):
+    got = bench.traffic_from_profiles("write_bcast_440x5120_p8", 72089600)
+    text = (PROFILES / "write_bcast_440x5120_p8_counters.md").read_text()
+    recorded = re.search(r"[Kk]ernel source hash[^`]*`([0-9a-f]{16})`", text).group(1)
+    if recorded == bench.kernel_source_hash():
+        assert got is not None and 0.99 < got / 72089600 < 1.05
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 16)
+    assert bench.traffic_from_profiles("write_bcast_440x5120_p8", 72089600) is None
+
+
+def test_packet_byte_accounting():
+    n = 512 * 7168
+    # P = 8: read 2n + 2 * 3.5n, write 10n  ->  19n per rank
+    assert bench.packet_fused_bytes(8, n) == 19 * n
+    # P = 2: read 2n + 2 * 2n, write 10n -> 16n
+    assert bench.packet_fused_bytes(2, 1000) == 16 * 1000
+
+
+def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
+    import sys
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    try:
+        bench.main()
+    except SystemExit as e:
+        assert e.code == 2
+    else:
+        raise AssertionError("bench.py --gpus 2 did not exit")
+    assert "ONE GPU" in capsys.readouterr().err
