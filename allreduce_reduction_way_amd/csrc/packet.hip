@@ -82,12 +82,28 @@ __global__ __launch_bounds__(kThreads) void k_ll_encode(CodecArgs a) {
         store_word(a.words + w, make_word(load_pair(a.elems, 2 * w, a.n, a.aligned4), a.flag));
 }
 
+// Four words in flight per lane: 8-byte loads need many requests outstanding
+// to keep HBM busy.
 __global__ __launch_bounds__(kThreads) void k_ll_decode(CodecArgs a) {
+    constexpr int K = 4;
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < a.nwords; w += stride) {
-        uint64_t v;
-        if (!wait_word(a.words + w, a.flag, v, a.status, a.max_spins)) return;
-        store_pair(a.dst, 2 * w, a.n, a.aligned4, word_data(v));
+    for (int64_t w0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; w0 < a.nwords;
+         w0 += stride * K) {
+        uint64_t v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t w = w0 + k * stride;
+            v[k] = w < a.nwords ? load_word(a.words + w) : make_word(0, a.flag);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int64_t w = w0 + k * stride;
+            if (w >= a.nwords) continue;
+            if (word_flag(v[k]) != a.flag &&
+                !wait_word(a.words + w, a.flag, v[k], a.status, a.max_spins))
+                return;
+            store_pair(a.dst, 2 * w, a.n, a.aligned4, word_data(v[k]));
+        }
     }
 }
 
@@ -551,9 +567,14 @@ int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void
     a.aligned4 = aligned_to(dst, 4);
     a.status = static_cast<int32_t *>(ctrl);
     a.max_spins = max_spins ? max_spins : AR_DEFAULT_MAX_SPINS;
-    // A modest grid: decode may wait on a producer that needs CUs of its own.
-    int64_t blocks = (a.nwords + kThreads - 1) / kThreads;
-    if (blocks > (int64_t)dev.cus * 2) blocks = (int64_t)dev.cus * 2;
+    // At most half of what is resident at once: decode may wait on a
+    // producer that needs CUs of its own.
+    const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(&k_ll_decode));
+    if (per_cu <= 0) return AR_ELAUNCH;
+    int64_t cap = (int64_t)per_cu * dev.cus / 2;
+    if (cap < 1) cap = 1;
+    int64_t blocks = (a.nwords + 4 * kThreads - 1) / (4 * kThreads);
+    if (blocks > cap) blocks = cap;
     return launch(reinterpret_cast<const void *>(&k_ll_decode), (unsigned)blocks, kThreads, a,
                   stream);
 }
