@@ -410,6 +410,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cold-calls", type=int, default=20)
+    ap.add_argument("--per-call", type=int, default=50, help="event-pair calls per row")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -450,7 +452,8 @@ def main():
     h = rows[headline.name]
     log(f"headline {h.name}: {args.warmup} warm-up + {args.steps} timed steps")
     ms, wall = time_streamed(torch, stream, h.step, args.steps, args.warmup)
-    per_call = time_per_call(torch, stream, h.step, max(50, min(args.steps, 500)))
+    per_call = time_per_call(torch, stream, h.step,
+                             args.per_call if args.per_call != 50 else max(50, min(args.steps, 500)))
     # the kernel's mean launch duration over the timed region: one launch per step
     achieved = gbs(h.alg_bytes, ms * 1e3)
     traffic = traffic_from_profiles(headline.name, h.alg_bytes)
@@ -491,12 +494,12 @@ def main():
             log(f"row {name}")
             steps = max(20, min(args.steps, 2000 if row.alg_bytes < (64 << 20) else 200))
             ms_r, _ = time_streamed(torch, stream, row.step, steps, 10)
-            pc = time_per_call(torch, stream, row.step, 50)
+            pc = time_per_call(torch, stream, row.step, args.per_call)
             scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
             cold = time_per_call(torch, stream, row.step, args.cold_calls, scrub=scrub)
             del scrub
             us = ms_r * 1e3
-            graph_us = time_graph(torch, stream, row) if row.graphable else None
+            graph_us = time_graph(torch, stream, row) if row.graphable and not args.no_graph else None
             out_rows[name] = {
                 "graph_us_per_call": round(graph_us, 3) if graph_us else None,
                 "graph_gbs": round(gbs(row.alg_bytes, graph_us), 1) if graph_us else None,
@@ -522,7 +525,8 @@ def main():
         noop.step = noop.factory(int(stream.cuda_stream))
         floor_ms, _ = time_streamed(torch, stream, noop.step, 2000, 50)
         floor_pc = time_per_call(torch, stream, noop.step, 200)
-        out_rows["empty_kernel_floor"] = {"graph_us_per_call": round(time_graph(torch, stream, noop), 3),
+        out_rows["empty_kernel_floor"] = {"graph_us_per_call": None if args.no_graph else
+                                          round(time_graph(torch, stream, noop), 3),
                                           "streamed_us_per_call": round(floor_ms * 1e3, 3),
                                           "per_call_us": {k: round(v, 3) for k, v in floor_pc.items()}}
         result["rows"] = out_rows
