@@ -211,3 +211,20 @@ def test_epoch_flag_graph_replay_with_changing_inputs():
         for r in range(P):
             assert np.array_equal(to_host(outs[r]), want[r]), (rep, r)
         _check_images(scratch, images, rep)
+
+
+def test_three_op_two_byte_aligned_buffers():
+    P, n = 4, 4096 * 5 + 3
+    xs = I.make_inputs("uniform", P, n, seed=91)
+    ins = [Guarded(n, shift=1, init=x) for x in xs]
+    outs = [Guarded(n, shift=3) for _ in range(P)]
+    scratch = _scratch(P, n)
+    ctrl = ctrl_block()
+    announce("three-op, 2-byte-aligned inputs and outputs")
+    _three_op([g.view for g in ins], scratch, [o.view for o in outs], 1, ctrl, n=n)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == 0
+    want, img = O.packet_fused(xs, 1, _zero_images(P, n))
+    for r in range(P):
+        assert np.array_equal(outs[r].host(), want[r]) and outs[r].guards_intact()
+    _check_images(scratch, img, 0)

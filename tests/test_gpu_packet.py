@@ -298,3 +298,38 @@ def test_packet_fused_fifty_calls_rotating_flags():
             got = _images(scratch)
             for r in range(P):
                 assert np.array_equal(got[r], images[r]), (call, r)
+
+
+@pytest.mark.parametrize("in_shift,out_shift", [(1, 0), (0, 1), (1, 1), (3, 2)])
+def test_packet_fused_two_byte_aligned_buffers(in_shift, out_shift):
+    """Inputs or outputs that are only 2-byte aligned take the element-wise
+    path for the bf16 pairs; results and images stay bit-exact."""
+    P, n = 8, 8192 * 3 + 7
+    xs = I.make_inputs("uniform", P, n, seed=70 + in_shift)
+    ins = [Guarded(n, shift=in_shift, init=x) for x in xs]
+    outs = [Guarded(n, shift=out_shift) for _ in range(P)]
+    scratch = _scratch(P, n)
+    ctrl = ctrl_block()
+    announce(f"packet fused, element shifts in={in_shift} out={out_shift}")
+    ar.ar_packet_fused([g.view for g in ins], scratch, [o.view for o in outs], 1, ctrl)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == 0
+    want, img = O.packet_fused(xs, 1, [np.zeros(O.packet_scratch_bytes(P, n), np.uint8)
+                                       for _ in range(P)])
+    for r in range(P):
+        assert np.array_equal(outs[r].host(), want[r]) and outs[r].guards_intact()
+    got = _images(scratch)
+    for r in range(P):
+        assert np.array_equal(got[r], img[r])
+
+
+@pytest.mark.parametrize("n", [1, 2, 5, 4096 * 3 + 3])
+def test_ll_encode_from_two_byte_aligned_source(n):
+    rng = np.random.default_rng(n + 99)
+    y = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
+    src = Guarded(n, shift=1, init=y)
+    pk = torch.zeros(16 * O.ll_packets(n), dtype=torch.uint8, device=DEV)
+    announce(f"ll_encode from a 2-byte-aligned source n={n}")
+    ar.ar_ll_encode(src.view, pk, 77)
+    torch.cuda.synchronize()
+    assert np.array_equal(pk.cpu().numpy().view(np.uint32), O.ll_encode(y, 77))
