@@ -1,0 +1,111 @@
+/*
+ * c_abi_check.c -- drives libar.so from plain C with raw device pointers:
+ * no PyTorch, no Python in the call path.  Test helper, built by the
+ * package's build step and run by tests/test_gpu_c_abi.py.
+ *
+ * usage: c_abi_check P n in.bin out.bin
+ *   in.bin   P * n little-endian uint16 (bf16 bit patterns), rank-major
+ *   out.bin  written: the n-element result of ar_oneshot_write_bcast
+ * Exit status 0 when every call succeeds, the P write-mode outputs are
+ * identical, ar_oneshot_sum and a fused packet call (all ranks, flag 1) agree
+ * with them, and the packet call's control block reports no time-out.
+ */
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "ar.h"
+
+#define HIP_OK(x)                                                                  \
+    do {                                                                           \
+        hipError_t e_ = (x);                                                       \
+        if (e_ != hipSuccess) {                                                    \
+            fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));         \
+            return 2;                                                              \
+        }                                                                          \
+    } while (0)
+
+#define AR_OK_(x)                                                                  \
+    do {                                                                           \
+        int rc_ = (x);                                                             \
+        if (rc_ != AR_OK) {                                                        \
+            fprintf(stderr, "%s failed: %s\n", #x, ar_strerror(rc_));              \
+            return 3;                                                              \
+        }                                                                          \
+    } while (0)
+
+int main(int argc, char **argv)
+{
+    if (argc != 5) {
+        fprintf(stderr, "usage: %s P n in.bin out.bin\n", argv[0]);
+        return 1;
+    }
+    const int P = atoi(argv[1]);
+    const int64_t n = atoll(argv[2]);
+    if (P < 2 || P > AR_MAX_P || n <= 0) return 1;
+    const size_t bytes = (size_t)n * 2;
+
+    uint16_t *host = malloc(bytes * P), *res = malloc(bytes), *chk = malloc(bytes);
+    if (!host || !res || !chk) return 1;
+    FILE *f = fopen(argv[3], "rb");
+    if (!f || fread(host, 2, (size_t)n * P, f) != (size_t)n * P) return 1;
+    fclose(f);
+
+    ar_ptrs in = {{0}}, out = {{0}}, out2 = {{0}}, scratch = {{0}};
+    const int64_t sbytes = ar_packet_scratch_bytes(P, n);
+    for (int p = 0; p < P; ++p) {
+        HIP_OK(hipMalloc(&in.p[p], bytes));
+        HIP_OK(hipMalloc(&out.p[p], bytes));
+        HIP_OK(hipMalloc(&out2.p[p], bytes));
+        HIP_OK(hipMalloc(&scratch.p[p], (size_t)sbytes));
+        HIP_OK(hipMemcpy(in.p[p], host + (size_t)p * n, bytes, hipMemcpyHostToDevice));
+        HIP_OK(hipMemset(scratch.p[p], 0, (size_t)sbytes));
+    }
+    void *one = NULL, *ctrl = NULL;
+    HIP_OK(hipMalloc(&one, bytes));
+    HIP_OK(hipMalloc(&ctrl, AR_CTRL_BYTES));
+    HIP_OK(hipMemset(ctrl, 0, AR_CTRL_BYTES));
+    hipStream_t s;
+    HIP_OK(hipStreamCreate(&s));
+
+    AR_OK_(ar_oneshot_write_bcast(in, out, P, n, s));
+    AR_OK_(ar_oneshot_sum(in, one, P, n, s));
+    AR_OK_(ar_packet_fused(in, scratch, out2, P, 0, P, n, 1u, ctrl, 0, s));
+    HIP_OK(hipStreamSynchronize(s));
+
+    ar_ctrl c;
+    HIP_OK(hipMemcpy(&c, ctrl, sizeof c, hipMemcpyDeviceToHost));
+    if (c.status != AR_OK) {
+        fprintf(stderr, "packet call status %s\n", ar_strerror(c.status));
+        return 4;
+    }
+    HIP_OK(hipMemcpy(res, out.p[0], bytes, hipMemcpyDeviceToHost));
+    for (int p = 1; p < P; ++p) {
+        HIP_OK(hipMemcpy(chk, out.p[p], bytes, hipMemcpyDeviceToHost));
+        if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "write-mode output %d differs\n", p); return 5; }
+    }
+    HIP_OK(hipMemcpy(chk, one, bytes, hipMemcpyDeviceToHost));
+    if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "one-shot differs\n"); return 5; }
+    for (int p = 0; p < P; ++p) {
+        HIP_OK(hipMemcpy(chk, out2.p[p], bytes, hipMemcpyDeviceToHost));
+        if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "packet output %d differs\n", p); return 5; }
+    }
+    f = fopen(argv[4], "wb");
+    if (!f || fwrite(res, 2, (size_t)n, f) != (size_t)n) return 1;
+    fclose(f);
+
+    for (int p = 0; p < P; ++p) {
+        HIP_OK(hipFree(in.p[p]));
+        HIP_OK(hipFree(out.p[p]));
+        HIP_OK(hipFree(out2.p[p]));
+        HIP_OK(hipFree(scratch.p[p]));
+    }
+    HIP_OK(hipFree(one));
+    HIP_OK(hipFree(ctrl));
+    HIP_OK(hipStreamDestroy(s));
+    free(host); free(res); free(chk);
+    printf("c_abi_check: ok\n");
+    return 0;
+}
