@@ -128,7 +128,7 @@ struct FusedArgs {
     uint64_t max_spins;
 };
 
-// Words of slice j's slot that carry data (2 per packet).
+// Elements in slice j (the last slice absorbs the remainder).
 __device__ __forceinline__ int64_t slice_len(const FusedArgs &a, int j, int P) {
     return j == P - 1 ? a.n - (int64_t)(P - 1) * a.L : a.L;
 }

@@ -26,7 +26,8 @@ overhead);
 rocprofv3 in profiles/, scaled by the same counters' reading for a plain copy
 of known size, or null when the kernels changed after the counters were
 taken.  `cpu_baseline` times the CPU oracle (test infrastructure) on the full
-headline workload, single-threaded.
+headline workload, single-threaded, and (`cpu_baseline.rows`) on each row's
+own inputs for about 1.5 s each.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only-headline      (profiling runs: headline only)
@@ -82,6 +83,7 @@ class Row:
         self.name, self.alg_bytes, self.launches = name, alg_bytes, launches_per_step
         self.factory, self.note, self.graphable = factory, note, graphable
         self.step = None
+        self.host = None    # host copies of the inputs (the oracle's CPU timing)
         # The device buffers a row's launches (and captured graphs) address:
         # bound here too, so they live exactly as long as the row.
         self.keep = tuple(v for v in (factory.__defaults__ or ()) if v is not None)
@@ -109,9 +111,13 @@ def make_rows(names, torch, ar, I, W):
     dev = torch.device("cuda:0")
     P_ = ar._ptrs
 
+    host_inputs = {}
+
     def dev_inputs(w, seed=0):
         import numpy as np
-        return [torch.from_numpy(x.view(np.int16)).to(dev) for x in I.make_inputs(w.dist, w.P, w.n, seed)]
+        xs = I.make_inputs(w.dist, w.P, w.n, seed)
+        host_inputs[w.name] = xs     # the same inputs, for the oracle's CPU timing
+        return [torch.from_numpy(x.view(np.int16)).to(dev) for x in xs]
 
     def ctrl_block():
         return torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8, device=dev)
@@ -298,6 +304,9 @@ def make_rows(names, torch, ar, I, W):
                       "read 4 B (flags already in place), write 2 B per element", graphable=True)
             row.ctrl = ctrl
             rows[W.LL_DECODE_512x7168.name] = row
+        host_inputs[W.LL_DECODE_512x7168.name] = host_inputs[w.name]
+    for name, row in rows.items():
+        row.host = host_inputs.get(name)
     return rows
 
 
@@ -397,6 +406,60 @@ def cpu_baseline(xs_host, budget_s=12.0):
     return {"value": round(alg * calls / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"full 440x5120 x 8 write-mode share, {calls} calls in {el:.1f} s "
                       f"({1e3 * el / calls:.1f} ms/call), single thread"}
+
+
+def cpu_rows_leg(rows, W, budget_s=1.5):
+    """The oracle as it stands, single-threaded, on each row's own inputs:
+    milliseconds per call of the same work the row's step does on the GPU
+    (all ranks for the packet rows; all four owners for the 64 Mi two-shot)."""
+    import numpy as np
+    from oracle import oracle as O
+
+    def packet(xs):
+        return O.packet_fused(xs, 1, [np.zeros(O.packet_scratch_bytes(len(xs), xs[0].size),
+                                               np.uint8) for _ in xs])
+
+    def owners(xs):
+        outs = [np.zeros(xs[0].size, np.uint16) for _ in xs]
+        for r in range(len(xs)):
+            outs = O.twoshot_share(xs, r, outs)
+        return outs
+
+    # name -> (oracle call on the row's host inputs, divisor, what one call covers)
+    work = {
+        W.ONESHOT_4K.name: (lambda xs: O.oneshot_sum(xs), 1, "one call"),
+        W.WRITE_BCAST_440x5120.name: (lambda xs: O.write_bcast(xs), 1, "one call"),
+        W.PACKET_512x7168.name: (packet, 1, "all 8 ranks"),
+        W.PACKET_3OP_512x7168.name: (packet, 1, "all 8 ranks (one fused oracle call)"),
+        W.PACKET_EPOCH_GRAPH_512x7168.name: (packet, 1, "all 8 ranks"),
+        W.PACKET_RANK3_512x7168.name: (packet, 8, "all 8 ranks / 8"),
+        W.TWOSHOT_680x5120_R3.name: (lambda xs: O.twoshot_share(
+            xs, 3, [np.zeros(xs[0].size, np.uint16) for _ in xs]), 1, "rank 3's slice"),
+        W.TWOSHOT_64Mi_P4.name: (owners, 1, "all 4 owners"),
+        W.REDUCE_SCATTER_440x5120_R3.name: (lambda xs: O.reduce_scatter(xs, 3), 1, "rank 3's block"),
+        W.LL_ENCODE_512x7168.name: (lambda xs: O.ll_encode(xs[0], 1), 1, "one buffer"),
+    }
+    dec = rows.get(W.LL_DECODE_512x7168.name)
+    if dec is not None and dec.host is not None:
+        pk, n = O.ll_encode(dec.host[0], 1), dec.host[0].size
+        work[dec.name] = (lambda xs: O.ll_decode(pk, n, 1), 1, "one buffer")
+    out = {}
+    for name, row in rows.items():
+        if name not in work or row.host is None:
+            continue
+        fn, div, what = work[name]
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            fn(row.host)
+            calls += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or calls >= 500:
+                break
+        ms = 1e3 * el / calls / div
+        out[name] = {"oracle_ms_per_step": round(ms, 4),
+                     "oracle_gbs": round(gbs(row.alg_bytes, ms * 1e3), 3),
+                     "sample": f"{calls} oracle calls in {el:.2f} s, each {what}"}
+    return out
 
 
 # ------------------------------------------------------------------------ main
@@ -542,6 +605,14 @@ def main():
         torch.cuda.synchronize()
         y = O.oneshot_sum(xs)
         cb["gpu_output_matches"] = all(np.array_equal(t.cpu().numpy().view(np.uint16), y) for t in d_out)
+        if not args.only_headline:
+            log("cpu baseline per row (oracle)")
+            per_row = cpu_rows_leg(rows, W)
+            for name, v in per_row.items():
+                if name in result.get("rows", {}):
+                    us = result["rows"][name]["streamed_us_per_call"]
+                    v["gpu_speedup_streamed"] = round(v["oracle_ms_per_step"] * 1e3 / us, 1)
+            cb["rows"] = per_row
         result["cpu_baseline"] = cb
     else:
         result["cpu_baseline"] = None

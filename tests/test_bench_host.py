@@ -46,3 +46,22 @@ def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
     else:
         raise AssertionError("bench.py --gpus 2 did not exit")
     assert "ONE GPU" in capsys.readouterr().err
+
+
+def test_cpu_rows_leg_covers_every_workload():
+    """Every workload row gets an oracle timing; inputs here are small
+    stand-ins of the rows' shapes so the check runs in a second."""
+    import types
+
+    from allreduce_reduction_way_amd import inputs as I, workloads as W
+
+    rows = {}
+    for w in W.ALL:
+        P = w.P
+        n = 1024 * P
+        rows[w.name] = types.SimpleNamespace(name=w.name, alg_bytes=4 * n,
+                                             host=I.make_inputs("uniform", P, n, seed=1))
+    got = bench.cpu_rows_leg(rows, W, budget_s=0.01)
+    assert set(got) == {w.name for w in W.ALL}
+    for name, v in got.items():
+        assert v["oracle_ms_per_step"] > 0 and v["oracle_gbs"] > 0, name
