@@ -38,11 +38,13 @@ namespace {
 
 // Two bf16 starting at element e of a slice of `len` elements (e even, e < len
 // or the word is padding), packed low element first; elements past the slice
-// read as zero.
+// read as zero.  Every element is read once and written once per call, so
+// the aligned case takes non-temporal (streaming) accesses: they leave L2 and
+// the MALL to the packets, which are read back within the call.
 __device__ __forceinline__ uint32_t load_pair(const uint16_t *p, int64_t e, int64_t len,
                                               bool aligned4) {
     if (e + 1 < len) {
-        if (aligned4) return *reinterpret_cast<const uint32_t *>(p + e);
+        if (aligned4) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(p + e));
         return (uint32_t)p[e] | ((uint32_t)p[e + 1] << 16);
     }
     return e < len ? (uint32_t)p[e] : 0u;
@@ -52,7 +54,7 @@ __device__ __forceinline__ void store_pair(uint16_t *p, int64_t e, int64_t len, 
                                            uint32_t d) {
     if (e + 1 < len) {
         if (aligned4) {
-            *reinterpret_cast<uint32_t *>(p + e) = d;
+            __builtin_nontemporal_store(d, reinterpret_cast<uint32_t *>(p + e));
         } else {
             p[e] = (uint16_t)d;
             p[e + 1] = (uint16_t)(d >> 16);
@@ -63,6 +65,9 @@ __device__ __forceinline__ void store_pair(uint16_t *p, int64_t e, int64_t len, 
 }
 
 // ---- standalone encode / decode ----------------------------------------------
+//
+// (Non-temporal element accesses: decode of 512x7168 on MI355X runs 3.85 us
+// instead of 4.42 us per call; encode is unchanged at 3.9 us.)
 
 struct CodecArgs {
     const uint16_t *elems;  // encode: source; decode: unused
@@ -79,7 +84,8 @@ struct CodecArgs {
 __global__ __launch_bounds__(kThreads) void k_ll_encode(CodecArgs a) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t w = (int64_t)blockIdx.x * kThreads + threadIdx.x; w < a.nwords; w += stride)
-        store_word(a.words + w, make_word(load_pair(a.elems, 2 * w, a.n, a.aligned4), a.flag));
+        store_word(a.words + w,
+                   make_word(load_pair(a.elems, 2 * w, a.n, a.aligned4), a.flag));
 }
 
 // Four words in flight per lane: 8-byte loads need many requests outstanding
@@ -138,6 +144,11 @@ __device__ __forceinline__ int64_t slice_len(const FusedArgs &a, int j, int P) {
 // the step is issued before any store: on CDNA the vector-memory counter
 // covers loads and stores alike, so a load issued after a write-through store
 // would also wait for that store's acknowledgement.
+//
+// The element side takes non-temporal accesses (load_pair, store_pair), so it
+// does not push the scratch packets, which are read back within the call, out
+// of L2 and the MALL: 100.8 us instead of 111.3 us per call for 512x7168 x 8
+// on MI355X (the loads give most of it).
 //
 // CARRY: the rank's own contributions come from registers instead of being
 // read back from its own slots -- its scatter of chunk c into inbox_r[slot r]
@@ -235,10 +246,10 @@ __device__ __forceinline__ bool pipeline_step(const FusedArgs &a, uint32_t flag,
             res_d[k] = reduce_word<P>(dw);
             const uint64_t res = make_word(res_d[k], flag);
 #pragma unroll
-            for (int j = 0; j < P; ++j)
-                store_word(static_cast<uint64_t *>(a.scratch.p[j]) + (int64_t)(P + r) * a.slot_words +
-                               w,
-                           res);
+            for (int j = 0; j < P; ++j) {
+                uint64_t *resbox_j = static_cast<uint64_t *>(a.scratch.p[j]) + P * a.slot_words;
+                store_word(resbox_j + r * a.slot_words + w, res);
+            }
         }
     }
 
