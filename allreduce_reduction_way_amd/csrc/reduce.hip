@@ -53,8 +53,11 @@ __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
             const int64_t v = v0 + u * nthreads;
             if (v < a.nvec) {
                 const u32x4 r = reduce_vec<P>(x[u]);
+                // byte offset from the output pointer: below 2**31 (launch_reduce
+                // cuts longer ranges into pieces)
+                const uint32_t off = (uint32_t)(2 * (a.head + 8 * v));
 #pragma unroll
-                for (int o = 0; o < NOUT; ++o) store_vec(a.out.p[o], a.head + 8 * v, r);
+                for (int o = 0; o < NOUT; ++o) store_vec(a.out.p[o], off, r);
             }
         }
     }
@@ -140,11 +143,15 @@ void split_range(const ar_ptrs &in, const ar_ptrs &out, int P, int nout, int64_t
     a->ntail = len - head - 8 * a->nvec;
 }
 
-int launch_reduce(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast, int64_t len,
-                  void *stream) {
-    if (len == 0) return AR_OK;
-    DeviceInfo dev;
-    if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
+ar_ptrs offset_ptrs(const ar_ptrs &p, int count, int64_t elem) {
+    ar_ptrs r = {};
+    for (int k = 0; k < count; ++k) r.p[k] = static_cast<uint16_t *>(p.p[k]) + elem;
+    return r;
+}
+
+// One launch over a range of at most kPieceElems elements.
+int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast, int64_t len,
+                 bool ntl, const DeviceInfo &dev, void *stream) {
     ReduceArgs a;
     split_range(in_at, out_at, P, bcast ? P : 1, len, &a);
 
@@ -180,15 +187,30 @@ int launch_reduce(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast
     if (scalar_blocks > blocks) blocks = scalar_blocks;
     if (blocks > (int64_t)dev.cus * 16) blocks = (int64_t)dev.cus * 16;  // lanes loop beyond
     if (blocks < 1) blocks = 1;
-    const int64_t touched = (int64_t)(P + (bcast ? P : 1)) * len * 2;
-    ReduceKernel fn = pick(bcast, touched > kStreamingBytes, P, U);
+    ReduceKernel fn = pick(bcast, ntl, P, U);
     return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, (unsigned)threads, a, stream);
 }
 
-ar_ptrs offset_ptrs(const ar_ptrs &p, int count, int64_t elem) {
-    ar_ptrs r = {};
-    for (int k = 0; k < count; ++k) r.p[k] = static_cast<uint16_t *>(p.p[k]) + elem;
-    return r;
+// The kernel addresses its outputs with 32-bit byte offsets (see store_vec),
+// so a range longer than kPieceElems elements (1 GiB per buffer) is cut into
+// consecutive launches on the same stream.  The streaming decision is taken
+// for the whole call.
+constexpr int64_t kPieceElems = 1ll << 29;
+
+int launch_reduce(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast, int64_t len,
+                  void *stream) {
+    if (len == 0) return AR_OK;
+    DeviceInfo dev;
+    if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
+    const int nout = bcast ? P : 1;
+    const bool ntl = (int64_t)(P + nout) * len * 2 > kStreamingBytes;
+    for (int64_t b = 0; b < len; b += kPieceElems) {
+        const int64_t m = len - b < kPieceElems ? len - b : kPieceElems;
+        const int rc = launch_piece(offset_ptrs(in_at, P, b), offset_ptrs(out_at, nout, b), P,
+                                    bcast, m, ntl, dev, stream);
+        if (rc != AR_OK) return rc;
+    }
+    return AR_OK;
 }
 
 // Common checks: P, n, non-null 2-byte-aligned pointers.
