@@ -1,7 +1,8 @@
 // host.hip -- host-only entry points of libar.so (no GPU needed) plus the
 // per-device property cache and the empty-kernel launch.
+#include <map>
 #include <mutex>
-#include <unordered_map>
+#include <utility>
 
 #include "host.h"
 
@@ -13,7 +14,7 @@ constexpr int kMaxDevices = 64;
 
 std::mutex g_mu;
 int g_cus[kMaxDevices];  // 0 = not queried yet
-std::unordered_map<uint64_t, int> g_occupancy;  // (device, kernel) -> blocks per CU
+std::map<std::pair<const void *, int>, int> g_occupancy;  // (kernel, device) -> blocks per CU
 
 __global__ void k_noop() {}
 
@@ -36,7 +37,7 @@ int current_device(DeviceInfo *out) {
 }
 
 int blocks_per_cu(const DeviceInfo &dev, const void *fn) {
-    const uint64_t key = (uint64_t)(uintptr_t)fn * kMaxDevices + (uint64_t)dev.device;
+    const std::pair<const void *, int> key(fn, dev.device);
     std::lock_guard<std::mutex> lock(g_mu);
     auto it = g_occupancy.find(key);
     if (it != g_occupancy.end()) return it->second;

@@ -263,8 +263,8 @@ int ar_noop(void *stream);
 /* Benchmark-only launch-shape overrides (process-global, not thread-safe).
  * ar_set_reduce_tuning: unroll (vectors in flight per lane) in {0 = automatic,
  * 1, 2, 4}, workgroup size in {0 = automatic, 64, 128, 256} and a cap on
- * workgroups (0 = automatic) for ar_oneshot_sum, ar_oneshot_write_bcast and
- * ar_twoshot_share.  ar_set_packet_tuning: workgroups per emulated rank of
+ * workgroups (0 = automatic) for ar_oneshot_sum, ar_oneshot_write_bcast,
+ * ar_twoshot_share and ar_reduce_scatter_share.  ar_set_packet_tuning: workgroups per emulated rank of
  * ar_packet_fused (0 = automatic; never more than fit on the device at once)
  * words per lane per chunk in {0 = automatic, 1, 2}, and the schedule of
  * ar_packet_fused: 0 = every workgroup runs all phases of its chunks as a
