@@ -1,4 +1,5 @@
-"""Every peer count P = 2..8 through every entry point: each P is its own
+"""Every peer count P = 2..8 through every entry point (and IEEE special
+values through every path): each P is its own
 template instantiation of the kernels, so each gets a bit-exact comparison
 with the CPU oracle on a ragged size that spans several chunks (and, for the
 packet paths, the full scratch image after two calls with rotating flags)."""
@@ -92,3 +93,58 @@ def test_packet_paths_every_P(P, path):
             assert np.array_equal(to_host(outs[r]), want[r]), (call, r)
         for r in range(P):
             assert np.array_equal(scratch[r].cpu().numpy(), images[r]), (call, r)
+
+
+def _special_inputs(P, n, seed):
+    """Arbitrary bit patterns with NaN, +-Inf, +-0, subnormals and extremes
+    planted: the packet path reduces through its own word routine."""
+    rng = np.random.default_rng(seed)
+    xs = [rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16) for _ in range(P)]
+    specials = np.array([0x0000, 0x8000, 0x7F80, 0xFF80, 0x7FC0, 0xFFC1, 0x0001, 0x8001, 0x007F,
+                         0x7F7F, 0xFF7F, 0x3F80, 0xBF80], dtype=np.uint16)
+    for x in xs:
+        idx = rng.integers(0, n, max(1, n // 6))
+        x[idx] = specials[rng.integers(0, specials.size, idx.size)]
+    return xs
+
+
+@pytest.mark.parametrize("P", [3, 8])
+def test_special_values_through_every_path(P):
+    n = _n(P)
+    xs = _special_inputs(P, n, seed=900 + P)
+    d_in = [to_dev(x) for x in xs]
+    y = O.oneshot_sum(xs)
+
+    announce(f"specials write_bcast P={P}")
+    outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ar.ar_oneshot_write_bcast(d_in, outs)
+    torch.cuda.synchronize()
+    for t in outs:
+        assert np.array_equal(to_host(t), y)
+
+    announce(f"specials twoshot P={P}, every owner")
+    two = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    for r in range(P):
+        ar.ar_twoshot_share(d_in, two, r)
+    torch.cuda.synchronize()
+    for t in two:
+        assert np.array_equal(to_host(t), y)
+
+    nb = O.packet_scratch_bytes(P, n)
+    for path in ("fused", "three_op"):
+        scratch = [torch.zeros(nb, dtype=torch.uint8, device=DEV) for _ in range(P)]
+        ctrl = ctrl_block()
+        outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+        announce(f"specials packet {path} P={P}")
+        if path == "fused":
+            ar.ar_packet_fused(d_in, scratch, outs, 1, ctrl)
+        else:
+            ar.ar_packet_send(d_in, scratch, 1, n=n)
+            ar.ar_packet_recv_reduce_send(scratch, n, 1, ctrl)
+            ar.ar_packet_recv(scratch, outs, 1, ctrl, n=n)
+        torch.cuda.synchronize()
+        assert ctrl_status(ctrl) == 0
+        want, images = O.packet_fused(xs, 1, [np.zeros(nb, np.uint8) for _ in range(P)])
+        for r in range(P):
+            assert np.array_equal(to_host(outs[r]), want[r]), (path, r)
+            assert np.array_equal(scratch[r].cpu().numpy(), images[r]), (path, r)
