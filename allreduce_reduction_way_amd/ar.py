@@ -154,7 +154,8 @@ def ar_ll_encode(src, dst_pkts, flag: int, n: int | None = None, stream=None) ->
 
 def ar_ll_decode(src_pkts, dst, flag: int, ctrl, n: int | None = None, max_spins: int = 0,
                  stream=None) -> None:
-    _check(lib().ar_ll_decode(_addr(src_pkts), _addr(dst), _n(n, [dst]), flag, _addr(ctrl),
+    _check(lib().ar_ll_decode(_addr(src_pkts), _addr(dst), _n(n, [dst]), flag,
+                              0 if ctrl is None else _addr(ctrl),
                               max_spins, _stream(stream)), "ar_ll_decode")
 
 

@@ -130,13 +130,17 @@ __device__ __forceinline__ uint64_t load_word(const uint64_t *p) {
 __device__ __forceinline__ uint32_t word_flag(uint64_t w) { return (uint32_t)(w >> 32); }
 __device__ __forceinline__ uint32_t word_data(uint64_t w) { return (uint32_t)w; }
 
-// Status word of the control block: agent-scope so every XCD sees it.
+// Status word of the control block: agent-scope so every XCD sees it.  A
+// null status (a decode called without a control block) reads as 0 and is
+// never raised.
 __device__ __forceinline__ int32_t load_status(const int32_t *s) {
+    if (!s) return 0;
     return __hip_atomic_load(const_cast<int32_t *>(s), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ void raise_status(int32_t *s, int32_t code) {
+    if (!s) return;
     int32_t expected = 0;
     __hip_atomic_compare_exchange_strong(s, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);

@@ -561,12 +561,15 @@ int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void
                  uint64_t max_spins, void *stream) {
     if (n < 0 || flag == 0) return AR_EINVAL;
     if (n == 0) return AR_OK;
-    if (!src_pkts || !dst || !ctrl || !aligned_to(dst, 2) || !aligned_to(src_pkts, 16) ||
-        !aligned_to(ctrl, 4))
+    if (!src_pkts || !dst || !aligned_to(dst, 2) || !aligned_to(src_pkts, 16) ||
+        (ctrl && !aligned_to(ctrl, 4)))
         return AR_EINVAL;
-    const Span sd = span_of(dst, 0, n, 2), sp = span_of(src_pkts, 0, ar_ll_packets(n), 16),
-               sc = span_of(ctrl, 0, AR_CTRL_BYTES, 1);
-    if (overlap(sd, sp) || overlap(sd, sc) || overlap(sp, sc)) return AR_EALIAS;
+    const Span sd = span_of(dst, 0, n, 2), sp = span_of(src_pkts, 0, ar_ll_packets(n), 16);
+    if (overlap(sd, sp)) return AR_EALIAS;
+    if (ctrl) {
+        const Span sc = span_of(ctrl, 0, AR_CTRL_BYTES, 1);
+        if (overlap(sd, sc) || overlap(sp, sc)) return AR_EALIAS;
+    }
     DeviceInfo dev;
     if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
     CodecArgs a = {};

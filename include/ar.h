@@ -163,7 +163,8 @@ int ar_ll_encode(const void *src, void *dst_pkts, int64_t n, uint32_t flag, void
 /* Wait until every packet at `src_pkts` carries `flag` in both flag words,
  * then decode n bf16 into `dst`.  Each packet word is polled at most
  * `max_spins` times (0 = AR_DEFAULT_MAX_SPINS); on timeout AR_ETIMEDOUT is
- * stored in ctrl->status and dst is undefined.  `ctrl` is required. */
+ * stored in ctrl->status and dst is undefined.  `ctrl` may be NULL: the waits
+ * stay bounded, but a timeout is then not reported (dst is undefined). */
 int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void *ctrl,
                  uint64_t max_spins, void *stream);
 

@@ -173,7 +173,8 @@ def test_codec_validation():
     assert _err(ar.ar_ll_encode, src, pk, 0, n=16, stream=STREAM) == ar.AR_EINVAL       # flag 0
     assert _err(ar.ar_ll_encode, src, pk + 8, 1, n=16, stream=STREAM) == ar.AR_EINVAL   # 16-B
     assert _err(ar.ar_ll_encode, src, src + 16, 1, n=16, stream=STREAM) == ar.AR_EALIAS
-    assert _err(ar.ar_ll_decode, pk, src, 1, 0, n=16, stream=STREAM) == ar.AR_EINVAL    # ctrl
+    assert _err(ar.ar_ll_decode, pk, src, 1, ctrl + 2, n=16, stream=STREAM) == ar.AR_EINVAL  # ctrl
+    ar.ar_ll_decode(pk, src, 1, None, n=0, stream=STREAM)                   # no control block
     assert _err(ar.ar_ll_decode, pk, src, 1, pk + 16, n=16, stream=STREAM) == ar.AR_EALIAS
     ar.ar_ll_encode(src, pk, 1, n=0, stream=STREAM)
     ar.ar_ll_decode(pk, src, 1, ctrl, n=0, stream=STREAM)

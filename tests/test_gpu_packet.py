@@ -80,6 +80,25 @@ def test_ll_round_trip_on_device_and_stale_flag_times_out():
     assert ctrl_status(ctrl) == ar.AR_ETIMEDOUT
 
 
+def test_ll_decode_without_control_block():
+    """ctrl = NULL: a decode of arrived packets works as usual, and one that
+    can never complete still ends after its bounded polls (nothing to report
+    the time-out to)."""
+    n = 4096 * 3 + 1
+    y = I.uniform_bf16(n, 2, 0)
+    pk = to_dev(O.ll_encode(y, 9).view(np.uint16))
+    out = Guarded(n)
+    announce("ll decode, no control block")
+    ar.ar_ll_decode(pk, out.view, 9, None)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.host(), y) and out.guards_intact()
+    announce("ll decode, no control block, stale flag, small spin bound")
+    stale = Guarded(n)
+    ar.ar_ll_decode(pk, stale.view, 10, None, max_spins=1024)
+    torch.cuda.synchronize()                     # returns: every wait is bounded
+    assert stale.guards_intact()
+
+
 def test_ll_decode_half_stale_packet_times_out():
     # one packet whose second flag word is stale: the packet is not arrived
     n = 4096
