@@ -481,9 +481,9 @@ int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const a
     const bool use_in = kind == kFused || kind == kFusedEpoch || kind == kSend || kind == kRoles;
     const bool use_out = kind == kFused || kind == kFusedEpoch || kind == kRecv || kind == kRoles;
     const bool use_ctrl = kind != kSend;
-    // Two words per lane per chunk: 120.8 us against 125.1 us with one word
-    // for 512x7168 x 8 on MI355X (fewer, wider chunks; 134 VGPRs, 3
-    // workgroups per CU, which the sweep showed to be enough).
+    // Two words per lane per chunk: 98.3 us against 111.4 us with one word
+    // for 512x7168 x 8 on MI355X (fewer, wider chunks; 155 VGPRs, 3
+    // workgroups per CU; fewer workgroups per rank than fit ran slower).
     const int wpl = g_fused_wpl_override ? g_fused_wpl_override : 2;
     FusedArgs a;
     int rc = prepare_packet(in, scratch, out, use_in, use_out, use_ctrl, P, rank_lo, rank_hi, n,
