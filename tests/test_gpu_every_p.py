@@ -148,3 +148,34 @@ def test_special_values_through_every_path(P):
         for r in range(P):
             assert np.array_equal(to_host(outs[r]), want[r]), (path, r)
             assert np.array_equal(scratch[r].cpu().numpy(), images[r]), (path, r)
+
+
+@pytest.mark.parametrize("P", [2, 8])
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 127, 128 * 8 - 1])
+def test_tiny_sizes_every_path(P, n):
+    """Degenerate sizes: fewer elements than one 128-element slice unit per
+    rank (L = 0: the last rank owns everything), a single packet, and a
+    partial last packet."""
+    xs = I.make_inputs("uniform", P, n, seed=1200 + n + P)
+    d_in = [to_dev(x) for x in xs]
+    y = O.oneshot_sum(xs)
+    announce(f"tiny n={n} P={P}: write_bcast, two-shot, packets")
+    outs = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ar.ar_oneshot_write_bcast(d_in, outs)
+    two = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    for r in range(P):
+        ar.ar_twoshot_share(d_in, two, r)
+    torch.cuda.synchronize()
+    for t in outs + two:
+        assert np.array_equal(to_host(t), y)
+    nb = O.packet_scratch_bytes(P, n)
+    scratch = [torch.zeros(nb, dtype=torch.uint8, device=DEV) for _ in range(P)]
+    ctrl = ctrl_block()
+    pk_out = [torch.zeros(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    ar.ar_packet_fused(d_in, scratch, pk_out, 1, ctrl)
+    torch.cuda.synchronize()
+    assert ctrl_status(ctrl) == 0
+    want, images = O.packet_fused(xs, 1, [np.zeros(nb, np.uint8) for _ in range(P)])
+    for r in range(P):
+        assert np.array_equal(to_host(pk_out[r]), want[r])
+        assert np.array_equal(scratch[r].cpu().numpy(), images[r])
