@@ -86,6 +86,22 @@ def test_oneshot_past_2_31_elements(shift):
     assert _equal_tiled(out, O.oneshot_sum(blk))
 
 
+def test_misaligned_inputs_past_2_31_elements():
+    """Inputs at element shifts 3 and 6 against aligned outputs: the scalar
+    path over the whole 32-bit-overflowing range."""
+    P, n = 2, BIG
+    blk = _blocks(P)
+    announce(f"large misaligned write_bcast P={P} n={n} (filling)")
+    ins = [_tiled(b, n, shift) for b, shift in zip(blk, (3, 6))]
+    outs = [torch.empty(n, dtype=torch.int16, device=DEV) for _ in range(P)]
+    announce(f"large misaligned write_bcast P={P} n={n} (kernel)")
+    ar.ar_oneshot_write_bcast(ins, outs)
+    torch.cuda.synchronize()
+    y = O.oneshot_sum(blk)
+    for o in outs:
+        assert _equal_tiled(o, y)
+
+
 def test_write_bcast_past_2_31_elements():
     P, n = 3, BIG
     blk = _blocks(P)

@@ -234,3 +234,65 @@ def test_streaming_size_takes_nontemporal_loads_and_matches(P, n, op):
         torch.cuda.synchronize()
         for t in outs:
             assert np.array_equal(to_host(t), y)
+
+
+# ------------------------------------------------- inputs misaligned to outputs
+
+@pytest.mark.parametrize("P,in_shifts,out_shift", [
+    (8, (0, 1, 2, 3, 4, 5, 6, 7), 0), (8, (7, 6, 5, 4, 3, 2, 1, 0), 5), (8, (3,) * 8, 0),
+    (2, (1, 0), 0), (2, (0, 7), 7), (3, (2, 4, 6), 1), (5, (1, 3, 5, 7, 0), 4)])
+@pytest.mark.parametrize("n", [1, 9, 1000, 4096 + 13, 100003])
+def test_inputs_misaligned_to_outputs(P, in_shifts, out_shift, n):
+    """Every input at its own element shift against the outputs (shifted by
+    `out_shift`): pointers with different addresses mod 16 take the scalar
+    path over the whole range."""
+    xs = _inputs(P, n, seed=n + P)
+    ins = [Guarded(n, shift=in_shifts[p], init=xs[p]) for p in range(P)]
+    y = O.oneshot_sum(xs)
+    announce(f"misaligned oneshot P={P} in={in_shifts} out={out_shift} n={n}")
+    out = Guarded(n, shift=out_shift)
+    ar.ar_oneshot_sum([g.view for g in ins], out.view)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.host(), y) and out.guards_intact()
+    announce(f"misaligned write_bcast P={P} in={in_shifts} out={out_shift} n={n}")
+    outs = [Guarded(n, shift=out_shift) for _ in range(P)]
+    ar.ar_oneshot_write_bcast([g.view for g in ins], [o.view for o in outs])
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.host(), y) and o.guards_intact()
+    announce(f"misaligned twoshot P={P} in={in_shifts} out={out_shift} n={n}")
+    two = [Guarded(n, shift=out_shift, init=np.full(n, 0x3C3C, np.uint16)) for _ in range(P)]
+    for r in range(P):
+        ar.ar_twoshot_share([g.view for g in ins], [o.view for o in two], r)
+    torch.cuda.synchronize()
+    for o in two:
+        assert np.array_equal(o.host(), y) and o.guards_intact()
+
+
+@pytest.mark.parametrize("P", [2, 8])
+def test_reduce_scatter_blocks_misaligned(P):
+    """Block offsets r * recvcount with recvcount odd put every rank's block
+    at a different alignment from the output."""
+    rc = 4096 + 3
+    xs = _inputs(P, P * rc, seed=77)
+    d_in = [to_dev(x) for x in xs]
+    for r in range(P):
+        out = Guarded(rc, shift=r % 3)
+        announce(f"misaligned reduce_scatter P={P} rank={r}")
+        ar.ar_reduce_scatter_share(d_in, out.view, r, recvcount=rc)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.host(), O.reduce_scatter(xs, r)) and out.guards_intact()
+
+
+def test_streaming_size_with_misaligned_inputs():
+    """Past 128 MiB touched the loads are non-temporal: misaligned inputs too."""
+    P, n = 3, (24 << 20) + 5
+    xs = I.make_inputs("uniform", P, n, seed=5)
+    ins = [Guarded(n, shift=s, init=x) for s, x in zip((1, 4, 0), xs)]
+    outs = [Guarded(n, shift=2) for _ in range(P)]
+    announce(f"misaligned streaming write_bcast P={P} n={n}")
+    ar.ar_oneshot_write_bcast([g.view for g in ins], [o.view for o in outs])
+    torch.cuda.synchronize()
+    y = O.oneshot_sum(xs)
+    for o in outs:
+        assert np.array_equal(o.host(), y) and o.guards_intact()
