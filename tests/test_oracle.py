@@ -3,7 +3,8 @@
 Each test checks the oracle against something the mathematics or the pages
 fix: closed forms, hand-derived IEEE 754 corner cases, an exact-rational model
 of binary32/bf16 rounding built from the standard's definitions, a library
-cast on inputs whose sum is exact, hand-derived packet and slice tables, and
+cast on inputs whose sum is exact, library binary32 adds and bf16 cast on
+arbitrary bit patterns, hand-derived packet and slice tables, and
 invariants of the fused packet path.  A dropped term, a wrong rank or element
 index, a swapped operand or a wrong rounding rule fails at least one of them.
 """
@@ -139,6 +140,33 @@ def test_position_fill_equals_library_cast_of_exact_sum(P):
     expected = exact.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert (O.oneshot_sum(xs) == expected).all()
     assert (O.oneshot_sum(xs[::-1]) == expected).all()
+
+
+# ------------------------------ library binary32 adds and library bf16 cast
+
+@pytest.mark.parametrize("P", [2, 3, 8])
+def test_library_adds_and_cast_on_arbitrary_bit_patterns(P):
+    # numpy's elementwise binary32 additions are IEEE round-to-nearest-even
+    # with subnormals kept; torch's binary32 -> bf16 conversion rounds to
+    # nearest even.  Summing in rank order with the one and converting with
+    # the other gives the definition independently of the oracle's code, on
+    # 200,000 arbitrary bit patterns per input (NaN, Inf, zeros and
+    # subnormals included).  NaN results are compared by NaN-ness only (the
+    # library keeps a payload; the definition stores 0x7FC0).
+    rng = np.random.default_rng(2024 + P)
+    n = 200_000
+    xs = [rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16) for _ in range(P)]
+    widened = [(x.astype(np.uint32) << 16).view(np.float32) for x in xs]
+    acc = widened[0].copy()
+    with np.errstate(invalid="ignore", over="ignore"):
+        for w in widened[1:]:
+            acc = acc + w
+    expected = torch.from_numpy(acc).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = O.oneshot_sum(xs)
+    nan = np.isnan(acc)
+    assert nan.any() and (~nan).sum() > n // 2
+    assert np.array_equal(got[~nan], expected[~nan])
+    assert (got[nan] == 0x7FC0).all()
 
 
 # --------------------------------------------------------------- write mode
