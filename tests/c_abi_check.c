@@ -7,10 +7,15 @@
  *   in.bin   P * n little-endian uint16 (bf16 bit patterns), rank-major
  *   out.bin  written: the n-element result of ar_oneshot_write_bcast
  * Exit status 0 when every call succeeds, the P write-mode outputs are
- * identical, ar_oneshot_sum and a fused packet call (all ranks, flag 1) agree
- * with them, and the packet call's control block reports no time-out.
+ * identical, and every other entry point agrees with them: ar_oneshot_sum,
+ * ar_twoshot_share (every owner), ar_reduce_scatter_share (every block of
+ * the first P * floor(n / P) elements), ar_ll_encode + ar_ll_decode of the
+ * result, a fused packet call (all ranks, flag 1), the three-launch packet
+ * decomposition (flag 2) and the epoch variant (flag 3), with no time-out in
+ * any control block.
  */
 #include <hip/hip_runtime_api.h>
+#include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -91,6 +96,63 @@ int main(int argc, char **argv)
     for (int p = 0; p < P; ++p) {
         HIP_OK(hipMemcpy(chk, out2.p[p], bytes, hipMemcpyDeviceToHost));
         if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "packet output %d differs\n", p); return 5; }
+    }
+
+    /* two-shot: every owner in turn fills its slice of every output */
+    for (int p = 0; p < P; ++p) HIP_OK(hipMemset(out2.p[p], 0, bytes));
+    for (int r = 0; r < P; ++r) AR_OK_(ar_twoshot_share(in, out2, P, r, n, s));
+    HIP_OK(hipStreamSynchronize(s));
+    for (int p = 0; p < P; ++p) {
+        HIP_OK(hipMemcpy(chk, out2.p[p], bytes, hipMemcpyDeviceToHost));
+        if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "two-shot output %d differs\n", p); return 5; }
+    }
+
+    /* reduce-scatter: block r of the first P * rc elements */
+    const int64_t rc = n / P;
+    for (int r = 0; r < P && rc > 0; ++r) {
+        AR_OK_(ar_reduce_scatter_share(in, one, P, r, rc, s));
+        HIP_OK(hipMemcpy(chk, one, (size_t)rc * 2, hipMemcpyDeviceToHost));
+        if (memcmp(chk, res + (size_t)r * rc, (size_t)rc * 2) != 0) {
+            fprintf(stderr, "reduce-scatter block %d differs\n", r);
+            return 5;
+        }
+    }
+
+    /* LL codec: encode the result, decode it without a control block */
+    void *pk = NULL;
+    HIP_OK(hipMalloc(&pk, (size_t)ar_ll_packets(n) * 16));
+    AR_OK_(ar_ll_encode(out.p[0], pk, n, 7u, s));
+    AR_OK_(ar_ll_decode(pk, one, n, 7u, NULL, 0, s));
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipMemcpy(chk, one, bytes, hipMemcpyDeviceToHost));
+    if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "codec round trip differs\n"); return 5; }
+    HIP_OK(hipFree(pk));
+
+    /* three-launch packet decomposition (flag 2), then the epoch kernel with
+     * the control block's epoch set to 2, so that it takes flag 3 and leaves
+     * the epoch at 3 */
+    AR_OK_(ar_packet_send(in, scratch, P, 0, P, n, 2u, s));
+    AR_OK_(ar_packet_recv_reduce_send(scratch, P, 0, P, n, 2u, ctrl, 0, s));
+    AR_OK_(ar_packet_recv(scratch, out2, P, 0, P, n, 2u, ctrl, 0, s));
+    HIP_OK(hipStreamSynchronize(s));
+    for (int p = 0; p < P; ++p) {
+        HIP_OK(hipMemcpy(chk, out2.p[p], bytes, hipMemcpyDeviceToHost));
+        if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "three-op output %d differs\n", p); return 5; }
+    }
+    const uint32_t epoch = 2u;
+    HIP_OK(hipMemcpy((char *)ctrl + offsetof(ar_ctrl, epoch), &epoch, sizeof epoch,
+                     hipMemcpyHostToDevice));
+    for (int p = 0; p < P; ++p) HIP_OK(hipMemset(out2.p[p], 0, bytes));
+    AR_OK_(ar_packet_fused_epoch(in, scratch, out2, P, 0, P, n, ctrl, 0, s));
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipMemcpy(&c, ctrl, sizeof c, hipMemcpyDeviceToHost));
+    if (c.status != AR_OK || c.epoch != 3u) {
+        fprintf(stderr, "epoch call: status %s, epoch %u\n", ar_strerror(c.status), c.epoch);
+        return 4;
+    }
+    for (int p = 0; p < P; ++p) {
+        HIP_OK(hipMemcpy(chk, out2.p[p], bytes, hipMemcpyDeviceToHost));
+        if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "epoch output %d differs\n", p); return 5; }
     }
     f = fopen(argv[4], "wb");
     if (!f || fwrite(res, 2, (size_t)n, f) != (size_t)n) return 1;

@@ -1,6 +1,6 @@
 """The C ABI driven from plain C (tests/c_abi_check.c): raw hipMalloc'd
 device pointers, one stream, no PyTorch in the call path.  The program checks
-that write mode, one-shot and the fused packet call agree; this test checks
+that every entry point agrees with write mode; this test checks
 its result against the CPU oracle."""
 from __future__ import annotations
 
