@@ -10,8 +10,11 @@ whole timed region).
 
 The same line also carries every other workload of the library (`rows`):
 one-shot 4096 x 8, the fused LL-packet share 512x7168 x 8 (graded launch of
-all eight ranks, flags rotating call to call), the two-shot share of rank 3
-at 680x5120 x 8, and the 4-owner two-shot at 64 Mi elements x 4.  Each row
+all eight ranks, flags rotating call to call), its three-launch
+decomposition, its device-epoch variant replayed from a HIP graph, rank 3's
+packet share alone, the two-shot share of rank 3 at 680x5120 x 8, the
+4-owner two-shot at 64 Mi elements x 4, rank 3's reduce-scatter block of
+440x5120 x 8, and the LL codec alone at 512x7168.  Each row
 reports the streamed time per call (N back-to-back calls / N), the device
 time per call from a captured graph of 100 calls, the per-call time with an
 event pair around each call, and the same after a 512 MiB read-only scrub
