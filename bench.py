@@ -87,6 +87,7 @@ class Row:
         self.factory, self.note, self.graphable = factory, note, graphable
         self.step = None
         self.host = None    # host copies of the inputs (the oracle's CPU timing)
+        self.outs = None    # device outputs of the last step (checked against the oracle)
         # The device buffers a row's launches (and captured graphs) address:
         # bound here too, so they live exactly as long as the row.
         self.keep = tuple(v for v in (factory.__defaults__ or ()) if v is not None)
@@ -138,6 +139,7 @@ def make_rows(names, torch, ar, I, W):
         rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, 1, f, "read P inputs + write P outputs",
                            graphable=True)
         rows[w.name].dev_inputs = ins
+        rows[w.name].outs = outs
     if W.ONESHOT_4K.name in names:
         w = W.ONESHOT_4K
         ins = dev_inputs(w)
@@ -149,6 +151,7 @@ def make_rows(names, torch, ar, I, W):
 
         rows[w.name] = Row(w.name, (w.P + 1) * w.n * 2, 1, f,
                            "latency-bound: compare with the empty-kernel floor", graphable=True)
+        rows[w.name].outs = [out]
     if W.PACKET_512x7168.name in names:
         w = W.PACKET_512x7168
         ins = dev_inputs(w)
@@ -171,6 +174,7 @@ def make_rows(names, torch, ar, I, W):
                   "graded launch: all 8 ranks; per rank 2n input + 4n(P-1)/P inbox + "
                   "4n(P-1)/P resbox read (own slots come from registers), 10n written")
         row.ctrl = ctrl
+        row.outs = outs
         rows[w.name] = row
     if W.TWOSHOT_680x5120_R3.name in names:
         w = W.TWOSHOT_680x5120_R3
@@ -184,6 +188,7 @@ def make_rows(names, torch, ar, I, W):
 
         rows[w.name] = Row(w.name, 2 * w.P * (e - b) * 2, 1, f,
                            "rank 3's slice: read P x slice, write P x slice", graphable=True)
+        rows[w.name].outs, rows[w.name].slice = outs, (b, e)
     if W.TWOSHOT_64Mi_P4.name in names:
         w = W.TWOSHOT_64Mi_P4
         ins = dev_inputs(w)
@@ -199,6 +204,7 @@ def make_rows(names, torch, ar, I, W):
 
         rows[w.name] = Row(w.name, 2 * w.P * w.n * 2, len(w.ranks), f,
                            "4 owner launches per step, full buffer into 4 outputs", graphable=True)
+        rows[w.name].outs = outs
     if W.PACKET_3OP_512x7168.name in names:
         w = W.PACKET_3OP_512x7168
         ins = dev_inputs(w)
@@ -223,6 +229,7 @@ def make_rows(names, torch, ar, I, W):
                   "send -> recv-reduce-send -> recv, one launch each; per rank 10n B read "
                   "(own slots read back: separate launches) + 10n B written")
         row.ctrl = ctrl
+        row.outs = outs
         rows[w.name] = row
     if W.PACKET_EPOCH_GRAPH_512x7168.name in names:
         w = W.PACKET_EPOCH_GRAPH_512x7168
@@ -247,6 +254,7 @@ def make_rows(names, torch, ar, I, W):
         row = Row(w.name, packet_fused_bytes(w.P, w.n) * w.P, 1, f,
                   "fused kernel, flag = device epoch + 1, replayed from a HIP graph")
         row.ctrl = ctrl
+        row.outs = outs
         rows[w.name] = row
     if W.REDUCE_SCATTER_440x5120_R3.name in names:
         w = W.REDUCE_SCATTER_440x5120_R3
@@ -260,6 +268,7 @@ def make_rows(names, torch, ar, I, W):
 
         rows[w.name] = Row(w.name, (w.P + 1) * rc * 2, 1, f,
                            "rank 3's block: read P x block, write 1 x block", graphable=True)
+        rows[w.name].outs = [out]
     if W.PACKET_RANK3_512x7168.name in names:
         w = W.PACKET_RANK3_512x7168
         ins = dev_inputs(w)
@@ -282,6 +291,7 @@ def make_rows(names, torch, ar, I, W):
                   "rank 3 alone, peers' packets staged: one rank's share of the packet path",
                   graphable=True)
         row.ctrl = ctrl
+        row.outs = outs
         rows[w.name] = row
     if W.LL_ENCODE_512x7168.name in names or W.LL_DECODE_512x7168.name in names:
         w = W.LL_ENCODE_512x7168
@@ -298,6 +308,7 @@ def make_rows(names, torch, ar, I, W):
 
             rows[w.name] = Row(w.name, 6 * w.n, 1, f, "read 2 B, write 4 B per element",
                                graphable=True)
+            rows[w.name].outs = [pk]
         if W.LL_DECODE_512x7168.name in names:
             def f(s, pk=pk, dst=dst, ctrl=ctrl, w=w):
                 c = _raw(ar, "ar_ll_decode", pk.data_ptr(), dst.data_ptr(), w.n, 1,
@@ -307,6 +318,7 @@ def make_rows(names, torch, ar, I, W):
             row = Row(W.LL_DECODE_512x7168.name, 6 * w.n, 1, f,
                       "read 4 B (flags already in place), write 2 B per element", graphable=True)
             row.ctrl = ctrl
+            row.outs = [dst]
             rows[W.LL_DECODE_512x7168.name] = row
         host_inputs[W.LL_DECODE_512x7168.name] = host_inputs[w.name]
     for name, row in rows.items():
@@ -478,6 +490,31 @@ def cpu_rows_leg(rows, W, budget_s=1.5):
     if dec is not None and dec.host is not None:
         pk, n = O.ll_encode(dec.host[0], 1), dec.host[0].size
         work[dec.name] = (lambda xs: O.ll_decode(pk, n, 1), 1, "one buffer")
+    def h16(t):
+        return t.cpu().numpy().view(np.uint16)
+
+    def matches(name, row, res):
+        """The row's device outputs after its timed steps against the oracle's
+        result on the same inputs (parity rechecked on the bench inputs)."""
+        o = getattr(row, "outs", None)
+        if name == W.WRITE_BCAST_440x5120.name:
+            return all(np.array_equal(h16(t), res[0]) for t in o)
+        if name in (W.ONESHOT_4K.name, W.REDUCE_SCATTER_440x5120_R3.name, W.LL_DECODE_512x7168.name):
+            return bool(np.array_equal(h16(o[0]), res))
+        if name == W.PACKET_RANK3_512x7168.name:
+            return bool(np.array_equal(h16(o[3]), res[0][3]))
+        if name in (W.PACKET_512x7168.name, W.PACKET_3OP_512x7168.name,
+                    W.PACKET_EPOCH_GRAPH_512x7168.name):
+            return all(np.array_equal(h16(t), want) for t, want in zip(o, res[0]))
+        if name == W.TWOSHOT_680x5120_R3.name:
+            b, e = row.slice
+            return all(np.array_equal(h16(t)[b:e], want[b:e]) for t, want in zip(o, res))
+        if name == W.TWOSHOT_64Mi_P4.name:
+            return all(np.array_equal(h16(t), want) for t, want in zip(o, res))
+        if name == W.LL_ENCODE_512x7168.name:
+            return bool(np.array_equal(o[0].cpu().numpy().view(np.uint32)[: res.size], res))
+        return None
+
     out = {}
     for name, row in rows.items():
         if name not in work or row.host is None:
@@ -485,7 +522,7 @@ def cpu_rows_leg(rows, W, budget_s=1.5):
         fn, div, what = work[name]
         calls, t0 = 0, time.perf_counter()
         while True:
-            fn(row.host)
+            res = fn(row.host)
             calls += 1
             el = time.perf_counter() - t0
             if el >= budget_s or calls >= 500:
@@ -493,7 +530,9 @@ def cpu_rows_leg(rows, W, budget_s=1.5):
         ms = 1e3 * el / calls / div
         out[name] = {"oracle_ms_per_step": round(ms, 4),
                      "oracle_gbs": round(gbs(row.alg_bytes, ms * 1e3), 3),
-                     "sample": f"{calls} oracle calls in {el:.2f} s, each {what}"}
+                     "sample": f"{calls} oracle calls in {el:.2f} s, each {what}",
+                     "gpu_output_matches": (None if getattr(row, "outs", None) is None
+                                            else matches(name, row, res))}
     return out
 
 
@@ -679,6 +718,8 @@ def main():
                     us = result["rows"][name]["streamed_us_per_call"]
                     v["gpu_speedup_streamed"] = round(v["oracle_ms_per_step"] * 1e3 / us, 1)
             cb["rows"] = per_row
+            cb["all_rows_match"] = all(v.get("gpu_output_matches") is not False
+                                       for v in per_row.values())
         result["cpu_baseline"] = cb
     else:
         result["cpu_baseline"] = None

@@ -65,3 +65,44 @@ def test_cpu_rows_leg_covers_every_workload():
     assert set(got) == {w.name for w in W.ALL}
     for name, v in got.items():
         assert v["oracle_ms_per_step"] > 0 and v["oracle_gbs"] > 0, name
+
+
+def test_cpu_rows_leg_rechecks_outputs_against_the_oracle():
+    """The parity recheck on bench inputs: outputs equal to the oracle's pass,
+    a single flipped element fails (CPU tensors stand in for device ones)."""
+    import types
+
+    import numpy as np
+    import torch
+
+    from allreduce_reduction_way_amd import inputs as I, workloads as W
+    from oracle import oracle as O
+
+    def t16(a):
+        return torch.from_numpy(np.array(a, dtype=np.uint16).view(np.int16))   # a copy
+
+    P, n = 8, 8 * 1024 + 8
+    xs = I.make_inputs("uniform", P, n, seed=3)
+    y = O.oneshot_sum(xs)
+    nb = O.packet_scratch_bytes(P, n)
+    pk_outs, _ = O.packet_fused(xs, 1, [np.zeros(nb, np.uint8) for _ in range(P)])
+    b, e = O.slice_range(P, n, 3)
+    rows = {
+        W.WRITE_BCAST_440x5120.name: types.SimpleNamespace(outs=[t16(y) for _ in range(P)]),
+        W.PACKET_512x7168.name: types.SimpleNamespace(outs=[t16(o) for o in pk_outs]),
+        W.TWOSHOT_680x5120_R3.name: types.SimpleNamespace(outs=[t16(y) for _ in range(P)],
+                                                          slice=(b, e)),
+        W.LL_ENCODE_512x7168.name: types.SimpleNamespace(
+            outs=[torch.from_numpy(O.ll_encode(xs[0], 1).view(np.uint8))]),
+        W.LL_DECODE_512x7168.name: types.SimpleNamespace(outs=[t16(xs[0])]),
+    }
+    for name, r in rows.items():
+        r.name, r.host, r.alg_bytes = name, xs, 4 * n
+    got = bench.cpu_rows_leg(rows, W, budget_s=0.0)
+    assert all(v["gpu_output_matches"] is True for v in got.values()), got
+    rows[W.PACKET_512x7168.name].outs[5][100] += 1
+    rows[W.TWOSHOT_680x5120_R3.name].outs[2][b + 7] += 1
+    got = bench.cpu_rows_leg(rows, W, budget_s=0.0)
+    assert got[W.PACKET_512x7168.name]["gpu_output_matches"] is False
+    assert got[W.TWOSHOT_680x5120_R3.name]["gpu_output_matches"] is False
+    assert got[W.WRITE_BCAST_440x5120.name]["gpu_output_matches"] is True
