@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
             "ar_packet_scratch_bytes": (i64, [i32, i64]),
             "ar_strerror": (ctypes.c_char_p, [i32]),
             "ar_noop": (i32, [vp]),
-            "ar_set_reduce_tuning": (i32, [i32, i32, i32]),
+            "ar_set_reduce_tuning": (i32, [i32, i32, i32, i32]),
             "ar_set_packet_tuning": (i32, [i32, i32, i32]),
         }
         for name, (res, args) in sig.items():
@@ -79,6 +79,18 @@ def lib() -> ctypes.CDLL:
 
 
 # ---------------------------------------------------------------- marshalling
+#
+# A torch tensor is checked before its address goes to the C library: it must
+# be contiguous, hold elements of the right width (2-byte bf16 / int16 /
+# uint16 for data, any type for byte buffers such as scratch, packets and
+# control blocks) and span at least the bytes the call touches.  The C side
+# cannot see sizes, so without this a short, strided or expanded tensor would
+# be read or written out of bounds.  An int is a raw device address that the
+# caller vouches for, passed as is.
+
+_ELEM_BYTES = 2
+_ELEM_DTYPES = ("torch.bfloat16", "torch.int16", "torch.uint16")
+
 
 def _addr(buf) -> int:
     """Device address of a torch CUDA tensor, or an int taken as an address."""
@@ -91,6 +103,33 @@ def _addr(buf) -> int:
 
 def _numel(buf) -> int:
     return int(buf.numel())
+
+
+def _require(buf, nbytes: int, what: str, elems: bool = False, word: int = 0) -> None:
+    """Raises ValueError unless the tensor `buf` is contiguous, has the element
+    type the argument takes and spans at least `nbytes` bytes.  `elems`: a bf16
+    data buffer; `word`: the exact element width (4 for a status word); else a
+    byte buffer of any element type."""
+    if isinstance(buf, int) or buf is None:
+        return
+    if not hasattr(buf, "element_size"):
+        raise TypeError(f"{what}: expected a CUDA tensor or a device address, "
+                        f"got {type(buf).__name__}")
+    if elems and str(buf.dtype) not in _ELEM_DTYPES:
+        raise ValueError(f"{what}: bf16 elements expected (bfloat16, int16 or uint16), "
+                         f"got {buf.dtype}")
+    if word and buf.element_size() != word:
+        raise ValueError(f"{what}: {word}-byte elements expected, got {buf.dtype}")
+    if not buf.is_contiguous():
+        raise ValueError(f"{what}: the tensor must be contiguous")
+    have = int(buf.numel()) * int(buf.element_size())
+    if have < nbytes:
+        raise ValueError(f"{what}: {have} bytes, the call touches {nbytes}")
+
+
+def _require_all(bufs: Sequence, nbytes: int, what: str, elems: bool = False) -> None:
+    for k, b in enumerate(bufs):
+        _require(b, nbytes, f"{what}[{k}]", elems=elems)
 
 
 def _stream(stream) -> int:
@@ -112,7 +151,19 @@ def _ptrs(bufs: Sequence) -> ar_ptrs:
 
 
 def _n(n, bufs) -> int:
-    return _numel(bufs[0]) if n is None else int(n)
+    if n is not None:
+        return int(n)
+    b = bufs[0]
+    if isinstance(b, int):
+        raise ValueError("n is required when buffers are raw addresses")
+    return _numel(b)
+
+
+def _scratch_bytes(P: int, n: int) -> int:
+    """Bytes of one rank's packet scratch, or 0 where the C call will reject
+    P or n itself."""
+    v = int(lib().ar_packet_scratch_bytes(P, n)) if n >= 0 else -1
+    return max(v, 0)
 
 
 def _check(rc: int, what: str) -> None:
@@ -123,24 +174,33 @@ def _check(rc: int, what: str) -> None:
 # ------------------------------------------------------------------ entry points
 
 def ar_oneshot_sum(inputs: Sequence, out, n: int | None = None, stream=None) -> None:
-    _check(lib().ar_oneshot_sum(_ptrs(inputs), _addr(out), len(inputs), _n(n, inputs),
-                                _stream(stream)), "ar_oneshot_sum")
+    n = _n(n, inputs)
+    _require_all(inputs, _ELEM_BYTES * n, "inputs", elems=True)
+    _require(out, _ELEM_BYTES * n, "out", elems=True)
+    _check(lib().ar_oneshot_sum(_ptrs(inputs), _addr(out), len(inputs), n, _stream(stream)),
+           "ar_oneshot_sum")
 
 
 def ar_oneshot_write_bcast(inputs: Sequence, outputs: Sequence, n: int | None = None,
                            stream=None) -> None:
     if len(outputs) != len(inputs):
         raise ValueError("write mode needs one output per input")
-    _check(lib().ar_oneshot_write_bcast(_ptrs(inputs), _ptrs(outputs), len(inputs),
-                                        _n(n, inputs), _stream(stream)), "ar_oneshot_write_bcast")
+    n = _n(n, inputs)
+    _require_all(inputs, _ELEM_BYTES * n, "inputs", elems=True)
+    _require_all(outputs, _ELEM_BYTES * n, "outputs", elems=True)
+    _check(lib().ar_oneshot_write_bcast(_ptrs(inputs), _ptrs(outputs), len(inputs), n,
+                                        _stream(stream)), "ar_oneshot_write_bcast")
 
 
 def ar_twoshot_share(inputs: Sequence, outputs: Sequence, rank: int, n: int | None = None,
                      stream=None) -> None:
     if len(outputs) != len(inputs):
         raise ValueError("the two-shot share needs one output per input")
-    _check(lib().ar_twoshot_share(_ptrs(inputs), _ptrs(outputs), len(inputs), rank,
-                                  _n(n, inputs), _stream(stream)), "ar_twoshot_share")
+    n = _n(n, inputs)
+    _require_all(inputs, _ELEM_BYTES * n, "inputs", elems=True)
+    _require_all(outputs, _ELEM_BYTES * n, "outputs", elems=True)
+    _check(lib().ar_twoshot_share(_ptrs(inputs), _ptrs(outputs), len(inputs), rank, n,
+                                  _stream(stream)), "ar_twoshot_share")
 
 
 def ar_ll_packets(n: int) -> int:
@@ -148,15 +208,34 @@ def ar_ll_packets(n: int) -> int:
 
 
 def ar_ll_encode(src, dst_pkts, flag: int, n: int | None = None, stream=None) -> None:
-    _check(lib().ar_ll_encode(_addr(src), _addr(dst_pkts), _n(n, [src]), flag, _stream(stream)),
+    n = _n(n, [src])
+    _require(src, _ELEM_BYTES * n, "src", elems=True)
+    _require(dst_pkts, 16 * ar_ll_packets(n), "dst_pkts")
+    _check(lib().ar_ll_encode(_addr(src), _addr(dst_pkts), n, flag, _stream(stream)),
            "ar_ll_encode")
 
 
 def ar_ll_decode(src_pkts, dst, flag: int, ctrl, n: int | None = None, max_spins: int = 0,
                  stream=None) -> None:
-    _check(lib().ar_ll_decode(_addr(src_pkts), _addr(dst), _n(n, [dst]), flag,
+    n = _n(n, [dst])
+    _require(src_pkts, 16 * ar_ll_packets(n), "src_pkts")
+    _require(dst, _ELEM_BYTES * n, "dst", elems=True)
+    _require(ctrl, AR_CTRL_BYTES, "ctrl")
+    _check(lib().ar_ll_decode(_addr(src_pkts), _addr(dst), n, flag,
                               0 if ctrl is None else _addr(ctrl),
                               max_spins, _stream(stream)), "ar_ll_decode")
+
+
+def _packet_buffers(P, n, inputs=None, scratch=None, outputs=None, ctrl=None):
+    """Size, type and layout checks of a packet-path call's buffers."""
+    if inputs is not None:
+        _require_all(inputs, _ELEM_BYTES * n, "inputs", elems=True)
+    if scratch is not None:
+        _require_all(scratch, _scratch_bytes(P, n), "scratch")
+    if outputs is not None:
+        _require_all(outputs, _ELEM_BYTES * n, "outputs", elems=True)
+    if ctrl is not None:
+        _require(ctrl, AR_CTRL_BYTES, "ctrl")
 
 
 def ar_packet_fused(inputs: Sequence, scratch: Sequence, outputs: Sequence, flag: int, ctrl,
@@ -166,15 +245,21 @@ def ar_packet_fused(inputs: Sequence, scratch: Sequence, outputs: Sequence, flag
     if len(scratch) != P or len(outputs) != P:
         raise ValueError("the packet path needs P inputs, P scratch buffers and P outputs")
     hi = P if rank_hi is None else rank_hi
+    n = _n(n, inputs)
+    _packet_buffers(P, n, inputs, scratch, outputs, ctrl)
     _check(lib().ar_packet_fused(_ptrs(inputs), _ptrs(scratch), _ptrs(outputs), P, rank_lo, hi,
-                                 _n(n, inputs), flag, _addr(ctrl), max_spins, _stream(stream)),
+                                 n, flag, _addr(ctrl), max_spins, _stream(stream)),
            "ar_packet_fused")
 
 
 def ar_reduce_scatter_share(inputs: Sequence, out, rank: int, recvcount: int | None = None,
                             stream=None) -> None:
     P = len(inputs)
+    if recvcount is None and isinstance(out, int):
+        raise ValueError("recvcount is required when the output is a raw address")
     rc = _numel(out) if recvcount is None else int(recvcount)
+    _require_all(inputs, _ELEM_BYTES * P * rc, "inputs", elems=True)
+    _require(out, _ELEM_BYTES * rc, "out", elems=True)
     _check(lib().ar_reduce_scatter_share(_ptrs(inputs), _addr(out), P, rank, rc, _stream(stream)),
            "ar_reduce_scatter_share")
 
@@ -186,8 +271,10 @@ def ar_packet_fused_epoch(inputs: Sequence, scratch: Sequence, outputs: Sequence
     if len(scratch) != P or len(outputs) != P:
         raise ValueError("the packet path needs P inputs, P scratch buffers and P outputs")
     hi = P if rank_hi is None else rank_hi
+    n = _n(n, inputs)
+    _packet_buffers(P, n, inputs, scratch, outputs, ctrl)
     _check(lib().ar_packet_fused_epoch(_ptrs(inputs), _ptrs(scratch), _ptrs(outputs), P, rank_lo,
-                                       hi, _n(n, inputs), _addr(ctrl), max_spins, _stream(stream)),
+                                       hi, n, _addr(ctrl), max_spins, _stream(stream)),
            "ar_packet_fused_epoch")
 
 
@@ -197,8 +284,10 @@ def ar_packet_send(inputs: Sequence, scratch: Sequence, flag: int, rank_lo: int 
     if len(scratch) != P:
         raise ValueError("need P scratch buffers")
     hi = P if rank_hi is None else rank_hi
-    _check(lib().ar_packet_send(_ptrs(inputs), _ptrs(scratch), P, rank_lo, hi, _n(n, inputs),
-                                flag, _stream(stream)), "ar_packet_send")
+    n = _n(n, inputs)
+    _packet_buffers(P, n, inputs, scratch)
+    _check(lib().ar_packet_send(_ptrs(inputs), _ptrs(scratch), P, rank_lo, hi, n, flag,
+                                _stream(stream)), "ar_packet_send")
 
 
 def ar_packet_recv_reduce_send(scratch: Sequence, n: int, flag: int, ctrl, rank_lo: int = 0,
@@ -206,7 +295,9 @@ def ar_packet_recv_reduce_send(scratch: Sequence, n: int, flag: int, ctrl, rank_
                                stream=None) -> None:
     P = len(scratch)
     hi = P if rank_hi is None else rank_hi
-    _check(lib().ar_packet_recv_reduce_send(_ptrs(scratch), P, rank_lo, hi, int(n), flag,
+    n = int(n)
+    _packet_buffers(P, n, None, scratch, None, ctrl)
+    _check(lib().ar_packet_recv_reduce_send(_ptrs(scratch), P, rank_lo, hi, n, flag,
                                             _addr(ctrl), max_spins, _stream(stream)),
            "ar_packet_recv_reduce_send")
 
@@ -218,8 +309,10 @@ def ar_packet_recv(scratch: Sequence, outputs: Sequence, flag: int, ctrl, rank_l
     if len(outputs) != P:
         raise ValueError("need P outputs")
     hi = P if rank_hi is None else rank_hi
-    _check(lib().ar_packet_recv(_ptrs(scratch), _ptrs(outputs), P, rank_lo, hi, _n(n, outputs),
-                                flag, _addr(ctrl), max_spins, _stream(stream)), "ar_packet_recv")
+    n = _n(n, outputs)
+    _packet_buffers(P, n, None, scratch, outputs, ctrl)
+    _check(lib().ar_packet_recv(_ptrs(scratch), _ptrs(outputs), P, rank_lo, hi, n, flag,
+                                _addr(ctrl), max_spins, _stream(stream)), "ar_packet_recv")
 
 
 def ar_slice_range(P: int, rank: int, n: int) -> tuple:
@@ -248,8 +341,10 @@ def ar_noop(stream=None) -> None:
     _check(lib().ar_noop(_stream(stream)), "ar_noop")
 
 
-def ar_set_reduce_tuning(unroll: int = 0, threads: int = 0, max_blocks: int = 0) -> None:
-    _check(lib().ar_set_reduce_tuning(unroll, threads, max_blocks), "ar_set_reduce_tuning")
+def ar_set_reduce_tuning(unroll: int = 0, threads: int = 0, max_blocks: int = 0,
+                         schedule: int = 0) -> None:
+    _check(lib().ar_set_reduce_tuning(unroll, threads, max_blocks, schedule),
+           "ar_set_reduce_tuning")
 
 
 def ar_set_packet_tuning(per_rank: int = 0, words_per_lane: int = 0, schedule: int = 0) -> None:

@@ -47,5 +47,21 @@ def build(verbose: bool = False) -> pathlib.Path:
     return LIB
 
 
+def build_c_program(src: pathlib.Path, exe: pathlib.Path, verbose: bool = False) -> pathlib.Path:
+    """Compile a plain C program that calls libar.so through include/ar.h
+    (gcc, C11, no HIP compiler): linked against libar.so and the HIP runtime,
+    with an rpath to the library beside it in this package."""
+    rocm = pathlib.Path("/opt/rocm")
+    rel = pathlib.Path(*[".."] * len(exe.resolve().parent.relative_to(ROOT).parts)) / PKG.name
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           f"-I{rocm / 'include'}", f"-I{ROOT / 'include'}", str(src), "-o", str(exe),
+           f"-L{PKG}", "-lar", f"-L{rocm / 'lib'}", "-lamdhip64",
+           f"-Wl,-rpath,$ORIGIN/{rel}", f"-Wl,-rpath,{rocm / 'lib'}"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return exe
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

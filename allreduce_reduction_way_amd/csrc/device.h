@@ -96,10 +96,19 @@ __device__ __forceinline__ u32x4 load_vec(const void *base, int64_t elem) {
 //
 // The store goes through a buffer resource so the policy can be chosen:
 // `base` must be the same for every lane of the wavefront (a kernel argument)
-// and `byte_off`, the lane's offset from it, below 2**31.
+// and `byte_off + 16`, the end of the lane's store, at most kStoreRangeBytes.
+// The hardware drops (does not fault on) a buffer store past the resource's
+// range, so every caller must keep its offsets inside it.
+constexpr uint32_t kStoreRangeBytes = 0x7FFFFFFFu;
+// An offset whose 16-byte store lies wholly past the range: the hardware
+// drops it.  Used on purpose for lanes with nothing to store, so that the
+// store instruction need not sit behind a branch.
+constexpr uint32_t kDroppedStoreOffset = 0x80000000u;
+static_assert(kDroppedStoreOffset >= kStoreRangeBytes, "a dropped store must be out of range");
+
 __device__ __forceinline__ void store_vec(void *base, uint32_t byte_off, u32x4 v) {
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kStoreRangeBytes, 0x00020000);
     __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 18);
 }
 

@@ -12,12 +12,15 @@
 namespace ar {
 
 constexpr int kThreads = 256;  // four 64-lane wavefronts per workgroup
+constexpr int kMaxDevices = 64;  // per-device host caches hold this many GPUs
 
 inline bool valid_P(int P) { return P >= 2 && P <= AR_MAX_P; }
 
 inline uintptr_t addr(const void *p) { return reinterpret_cast<uintptr_t>(p); }
 
 inline bool aligned_to(const void *p, uintptr_t a) { return (addr(p) & (a - 1)) == 0; }
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
 // A byte range [lo, lo + bytes) of one buffer argument.
 struct Span {

@@ -10,8 +10,6 @@ namespace ar {
 
 namespace {
 
-constexpr int kMaxDevices = 64;
-
 std::mutex g_mu;
 int g_cus[kMaxDevices];  // 0 = not queried yet
 std::map<std::pair<const void *, int>, int> g_occupancy;  // (kernel, device) -> blocks per CU

@@ -32,39 +32,47 @@ struct ReduceArgs {
     int64_t ntail;  // scalar elements after the bulk
 };
 
-template <int P, bool BCAST, int U, bool NTL>
-__global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
-    constexpr int NOUT = BCAST ? P : 1;
-    const int64_t nthreads = (int64_t)gridDim.x * blockDim.x;
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-
-    for (int64_t v0 = tid; v0 < a.nvec; v0 += nthreads * U) {
-        u32x4 x[U][P];
+// Loads, for each u < U, the 16-byte vector v + u * nth of every input into
+// x[u] (vectors past the bulk are skipped).
+template <int P, int U, bool NTL>
+__device__ __forceinline__ void load_stage(const ReduceArgs &a, int64_t v, int64_t nth,
+                                           u32x4 (&x)[U][P]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t v = v0 + u * nthreads;
-            if (v < a.nvec) {
+    for (int u = 0; u < U; ++u) {
+        const int64_t w = v + u * nth;
+        if (w < a.nvec) {
 #pragma unroll
-                for (int p = 0; p < P; ++p) x[u][p] = load_vec<NTL>(a.in.p[p], a.head + 8 * v);
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t v = v0 + u * nthreads;
-            if (v < a.nvec) {
-                const u32x4 r = reduce_vec<P>(x[u]);
-                // byte offset from the output pointer: below 2**31 (launch_reduce
-                // cuts longer ranges into pieces)
-                const uint32_t off = (uint32_t)(2 * (a.head + 8 * v));
-#pragma unroll
-                for (int o = 0; o < NOUT; ++o) store_vec(a.out.p[o], off, r);
-            }
+            for (int p = 0; p < P; ++p) x[u][p] = load_vec<NTL>(a.in.p[p], a.head + 8 * w);
         }
     }
+}
 
-    // Scalar elements: the head [0, head) and the tail after the bulk.
+// Reduces x[u] in rank order and stores the result at vector v + u * nth of
+// the output (one-shot) or of every output (write mode).
+template <int P, bool BCAST, int U>
+__device__ __forceinline__ void store_stage(const ReduceArgs &a, int64_t v, int64_t nth,
+                                            const u32x4 (&x)[U][P]) {
+    constexpr int NOUT = BCAST ? P : 1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t w = v + u * nth;
+        if (w < a.nvec) {
+            const u32x4 r = reduce_vec<P>(x[u]);
+            // byte offset from the output pointer: inside the store range
+            // (launch_reduce cuts longer ranges into pieces)
+            const uint32_t off = (uint32_t)(2 * (a.head + 8 * w));
+#pragma unroll
+            for (int o = 0; o < NOUT; ++o) store_vec(a.out.p[o], off, r);
+        }
+    }
+}
+
+// Scalar elements: the head [0, head) and the tail after the bulk.
+template <int P, bool BCAST>
+__device__ __forceinline__ void scalar_part(const ReduceArgs &a, int64_t tid, int64_t nth) {
+    constexpr int NOUT = BCAST ? P : 1;
     const int64_t nscalar = a.head + a.ntail;
-    for (int64_t s = tid; s < nscalar; s += nthreads) {
+    for (int64_t s = tid; s < nscalar; s += nth) {
         const int64_t i = s < a.head ? s : a.head + 8 * a.nvec + (s - a.head);
         uint16_t e[P];
 #pragma unroll
@@ -75,12 +83,96 @@ __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
     }
 }
 
+// Batches: each pass loads U vectors per input, then reduces and stores them.
+// The next pass's loads are issued after this pass's stores, and CDNA's
+// vector-memory counter retires loads and stores in issue order, so waiting
+// for those loads also waits for the stores to be acknowledged.
+template <int P, bool BCAST, int U, bool NTL>
+__global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
+    const int64_t nth = (int64_t)gridDim.x * blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (int64_t v0 = tid; v0 < a.nvec; v0 += nth * U) {
+        u32x4 x[U][P];
+        load_stage<P, U, NTL>(a, v0, nth, x);
+        store_stage<P, BCAST, U>(a, v0, nth, x);
+    }
+    scalar_part<P, BCAST>(a, tid, nth);
+}
+
+// Software pipeline, straight-line: workgroup b owns the S x U x blockDim.x
+// consecutive vectors from b x S x U x blockDim.x, taken in S stages of U per
+// lane.  The loads of stage k+1 are issued before the stores of stage k, so
+// the wait for stage k+1's data leaves stage k's stores in flight: reads of
+// one stage overlap writes of the previous one.  No memory instruction sits
+// behind a branch (a skipped instruction on one path would make the compiler
+// count conservatively and wait for the stores as well): lanes past the bulk
+// load the last vector again (in bounds) and store at an offset past the
+// buffer resource's range, which the hardware drops.
+template <int P, int U, bool NTL>
+__device__ __forceinline__ void load_stage_clamped(const ReduceArgs &a, int64_t v, int64_t bd,
+                                                   u32x4 (&x)[U][P]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int64_t w = v + u * bd;
+        w = w < a.nvec ? w : a.nvec - 1;
+#pragma unroll
+        for (int p = 0; p < P; ++p) x[u][p] = load_vec<NTL>(a.in.p[p], a.head + 8 * w);
+    }
+}
+
+template <int P, bool BCAST, int U>
+__device__ __forceinline__ void store_stage_masked(const ReduceArgs &a, int64_t v, int64_t bd,
+                                                   const u32x4 (&x)[U][P]) {
+    constexpr int NOUT = BCAST ? P : 1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t w = v + u * bd;
+        const u32x4 r = reduce_vec<P>(x[u]);
+        const uint32_t off = w < a.nvec ? (uint32_t)(2 * (a.head + 8 * w)) : kDroppedStoreOffset;
+#pragma unroll
+        for (int o = 0; o < NOUT; ++o) store_vec(a.out.p[o], off, r);
+    }
+}
+
+template <int P, bool BCAST, int U, int S, bool NTL>
+__global__ __launch_bounds__(kThreads) void k_reduce_pipe(ReduceArgs a) {
+    const int64_t bd = blockDim.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a.nvec > 0) {
+        const int64_t v0 = (int64_t)blockIdx.x * S * U * bd + threadIdx.x;
+        u32x4 x[2][U][P];
+        load_stage_clamped<P, U, NTL>(a, v0, bd, x[0]);
+#pragma unroll
+        for (int k = 0; k < S; ++k) {
+            if (k + 1 < S) load_stage_clamped<P, U, NTL>(a, v0 + (k + 1) * U * bd, bd, x[(k + 1) & 1]);
+            store_stage_masked<P, BCAST, U>(a, v0 + k * U * bd, bd, x[k & 1]);
+        }
+    }
+    scalar_part<P, BCAST>(a, tid, (int64_t)gridDim.x * blockDim.x);
+}
+
 // ---- kernel table ------------------------------------------------------------
 
 typedef void (*ReduceKernel)(ReduceArgs);
 
+// Schedules: kBatch grid-stride batches; kPipe2/4/8 pipelined, that many stages.
+enum Schedule { kBatch = 1, kPipe2 = 2, kPipe4 = 4, kPipe8 = 8 };
+
+inline bool is_pipe(int sched) { return sched == kPipe2 || sched == kPipe4 || sched == kPipe8; }
+
+template <int P, bool BCAST, bool NTL, int S>
+ReduceKernel pick_pipe_unroll(int U) {
+    return U == 1 ? k_reduce_pipe<P, BCAST, 1, S, NTL> : k_reduce_pipe<P, BCAST, 2, S, NTL>;
+}
+
 template <int P, bool BCAST, bool NTL>
-ReduceKernel pick_unroll(int U) {
+ReduceKernel pick_unroll(int U, int sched) {
+    switch (sched) {
+        case kPipe2: return pick_pipe_unroll<P, BCAST, NTL, 2>(U);
+        case kPipe4: return pick_pipe_unroll<P, BCAST, NTL, 4>(U);
+        case kPipe8: return pick_pipe_unroll<P, BCAST, NTL, 8>(U);
+        default: break;
+    }
     switch (U) {
         case 1: return k_reduce<P, BCAST, 1, NTL>;
         case 2: return k_reduce<P, BCAST, 2, NTL>;
@@ -89,21 +181,21 @@ ReduceKernel pick_unroll(int U) {
 }
 
 template <bool BCAST, bool NTL>
-ReduceKernel pick_p(int P, int U) {
+ReduceKernel pick_p(int P, int U, int sched) {
     switch (P) {
-        case 2: return pick_unroll<2, BCAST, NTL>(U);
-        case 3: return pick_unroll<3, BCAST, NTL>(U);
-        case 4: return pick_unroll<4, BCAST, NTL>(U);
-        case 5: return pick_unroll<5, BCAST, NTL>(U);
-        case 6: return pick_unroll<6, BCAST, NTL>(U);
-        case 7: return pick_unroll<7, BCAST, NTL>(U);
-        default: return pick_unroll<8, BCAST, NTL>(U);
+        case 2: return pick_unroll<2, BCAST, NTL>(U, sched);
+        case 3: return pick_unroll<3, BCAST, NTL>(U, sched);
+        case 4: return pick_unroll<4, BCAST, NTL>(U, sched);
+        case 5: return pick_unroll<5, BCAST, NTL>(U, sched);
+        case 6: return pick_unroll<6, BCAST, NTL>(U, sched);
+        case 7: return pick_unroll<7, BCAST, NTL>(U, sched);
+        default: return pick_unroll<8, BCAST, NTL>(U, sched);
     }
 }
 
-ReduceKernel pick(bool bcast, bool ntl, int P, int U) {
-    if (bcast) return ntl ? pick_p<true, true>(P, U) : pick_p<true, false>(P, U);
-    return ntl ? pick_p<false, true>(P, U) : pick_p<false, false>(P, U);
+ReduceKernel pick(bool bcast, bool ntl, int P, int U, int sched) {
+    if (bcast) return ntl ? pick_p<true, true>(P, U, sched) : pick_p<true, false>(P, U, sched);
+    return ntl ? pick_p<false, true>(P, U, sched) : pick_p<false, false>(P, U, sched);
 }
 
 // Bytes one launch touches beyond which its inputs take non-temporal loads:
@@ -114,6 +206,7 @@ constexpr int64_t kStreamingBytes = 128ll << 20;
 int g_unroll_override = 0;
 int g_threads_override = 0;
 int g_max_blocks_override = 0;
+int g_schedule_override = 0;  // 0 automatic, or a Schedule
 
 // Splits the range into scalar head, 16-byte bulk and scalar tail.  The bulk
 // exists only when every pointer has the same address mod 16.
@@ -155,19 +248,38 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
     ReduceArgs a;
     split_range(in_at, out_at, P, bcast ? P : 1, len, &a);
 
-    // Launch shape (swept on MI355X over workgroup size, unroll and grid):
-    //  - a small bulk (<= 256 lanes' worth per CU) is latency-bound: one vector
-    //    per lane in 64-lane workgroups, so the work spreads over every CU;
-    //  - a larger one takes 256-lane workgroups with two vectors in flight
-    //    per lane and exactly two workgroups per CU, looping (grid stride)
-    //    beyond that: a grid that is a multiple of the CU count keeps the
-    //    CUs evenly loaded (550 workgroups on 256 CUs ran 19% slower than 512).
-    int threads, U;
+    // Launch shape, chosen from sweeps on MI355X with the data coming from HBM
+    // (buffer sets rotated through 576 MB or more, and single calls after a
+    // 512 MiB scrub), by the bulk's 16-byte vectors per input:
+    //  - up to 256 per CU: latency-bound; one vector per lane in 64-lane
+    //    workgroups, so the work spreads over every CU;
+    //  - up to 768 per CU, P >= 4: the pipelined kernel in two stages, 64-lane
+    //    workgroups (1M elements x 8 / x 4: 6.2 / 3.9 us instead of 6.7 / 4.1);
+    //  - up to 2560 per CU, P = 8: one pass, four vectors per lane per input
+    //    (32 loads in flight per lane) in 64-lane workgroups, about one wave per
+    //    SIMD: the write-mode share of 440x5120 x 8 runs 14.0-14.4 us from HBM
+    //    instead of 15.1-15.9 us (13.4 instead of 15.9 us cold);
+    //  - beyond: 256-lane workgroups, two vectors in flight per lane, exactly
+    //    two workgroups per CU, grid stride (a grid that is a multiple of the
+    //    CU count keeps the CUs evenly loaded).
+    // With the data in the MALL instead (back-to-back calls on one buffer set
+    // of up to 256 MB) the last shape is faster (9.4 against 11.2 us for the
+    // 440x5120 x 8 share); the automatic choice is made for data from HBM.
+    int threads, U, sched = kBatch;
     int64_t blocks;
-    if (a.nvec <= (int64_t)dev.cus * kThreads) {
+    if (a.nvec <= (int64_t)dev.cus * 256) {
         threads = 64;
         U = 1;
         blocks = (a.nvec + threads - 1) / threads;
+    } else if (P >= 4 && a.nvec <= (int64_t)dev.cus * 768) {
+        threads = 64;
+        U = 1;
+        sched = kPipe2;
+        blocks = 0;  // set below: the pipelined grid covers the bulk
+    } else if (P == 8 && a.nvec <= (int64_t)dev.cus * 2560) {
+        threads = 64;
+        U = 4;
+        blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
     } else {
         threads = kThreads;
         U = 2;
@@ -182,12 +294,22 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
         threads = g_threads_override;
         blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
     }
-    if (g_max_blocks_override > 0 && blocks > g_max_blocks_override) blocks = g_max_blocks_override;
+    if (g_schedule_override != 0) sched = g_schedule_override;
+    if (is_pipe(sched)) {
+        // no grid stride: the grid covers the bulk, sched stages of U vectors per lane
+        if (U > 2) U = 2;
+        const int64_t per_block = (int64_t)threads * U * sched;
+        blocks = (a.nvec + per_block - 1) / per_block;
+    } else {
+        if (blocks == 0) blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
+        if (g_max_blocks_override > 0 && blocks > g_max_blocks_override)
+            blocks = g_max_blocks_override;
+        if (blocks > (int64_t)dev.cus * 16) blocks = (int64_t)dev.cus * 16;  // lanes loop beyond
+    }
     const int64_t scalar_blocks = (a.head + a.ntail + threads - 1) / threads;
     if (scalar_blocks > blocks) blocks = scalar_blocks;
-    if (blocks > (int64_t)dev.cus * 16) blocks = (int64_t)dev.cus * 16;  // lanes loop beyond
     if (blocks < 1) blocks = 1;
-    ReduceKernel fn = pick(bcast, ntl, P, U);
+    ReduceKernel fn = pick(bcast, ntl, P, U, sched);
     return launch(reinterpret_cast<const void *>(fn), (unsigned)blocks, (unsigned)threads, a, stream);
 }
 
@@ -196,6 +318,9 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
 // consecutive launches on the same stream.  The streaming decision is taken
 // for the whole call.
 constexpr int64_t kPieceElems = 1ll << 29;
+// the last 16-byte store of a piece ends at byte 2 * kPieceElems at most
+static_assert(2 * kPieceElems + 16 <= (int64_t)kStoreRangeBytes,
+              "a reduce piece must fit the output buffer resource's range");
 
 int launch_reduce(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast, int64_t len,
                   void *stream) {
@@ -289,13 +414,16 @@ int ar_reduce_scatter_share(ar_ptrs in, void *out, int P, int rank, int64_t recv
 }
 
 // Benchmark-only launch-shape override for the reduce entry points above.
-int ar_set_reduce_tuning(int unroll, int threads, int max_blocks) {
+int ar_set_reduce_tuning(int unroll, int threads, int max_blocks, int schedule) {
     if (!(unroll == 0 || unroll == 1 || unroll == 2 || unroll == 4) || max_blocks < 0 ||
-        !(threads == 0 || threads == 64 || threads == 128 || threads == 256))
+        !(threads == 0 || threads == 64 || threads == 128 || threads == 256) ||
+        !(schedule == 0 || schedule == kBatch || is_pipe(schedule)) ||
+        (is_pipe(schedule) && unroll == 4))
         return AR_EINVAL;
     g_unroll_override = unroll;
     g_threads_override = threads;
     g_max_blocks_override = max_blocks;
+    g_schedule_override = schedule;
     return AR_OK;
 }
 

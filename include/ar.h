@@ -263,15 +263,18 @@ int ar_noop(void *stream);
 
 /* Benchmark-only launch-shape overrides (process-global, not thread-safe).
  * ar_set_reduce_tuning: unroll (vectors in flight per lane) in {0 = automatic,
- * 1, 2, 4}, workgroup size in {0 = automatic, 64, 128, 256} and a cap on
- * workgroups (0 = automatic) for ar_oneshot_sum, ar_oneshot_write_bcast,
- * ar_twoshot_share and ar_reduce_scatter_share.  ar_set_packet_tuning: workgroups per emulated rank of
+ * 1, 2, 4}, workgroup size in {0 = automatic, 64, 128, 256}, a cap on
+ * workgroups (0 = automatic; batches only) and the schedule (0 = automatic,
+ * 1 = grid-stride batches: load U vectors, then store them; 2, 4 or 8 =
+ * pipelined in that many stages of U vectors per lane, the next stage's loads
+ * issued before the current stores, unroll 1 or 2) for ar_oneshot_sum,
+ * ar_oneshot_write_bcast, ar_twoshot_share and ar_reduce_scatter_share.  ar_set_packet_tuning: workgroups per emulated rank of
  * ar_packet_fused (0 = automatic; never more than fit on the device at once)
  * words per lane per chunk in {0 = automatic, 1, 2}, and the schedule of
  * ar_packet_fused: 0 = every workgroup runs all phases of its chunks as a
  * pipeline, 1 = separate scatter, reduce-broadcast and receive workgroups in
  * one grid.  Results do not depend on any of them. */
-int ar_set_reduce_tuning(int unroll, int threads, int max_blocks);
+int ar_set_reduce_tuning(int unroll, int threads, int max_blocks, int schedule);
 int ar_set_packet_tuning(int per_rank, int words_per_lane, int schedule);
 
 #ifdef __cplusplus

@@ -106,3 +106,136 @@ def test_cpu_rows_leg_rechecks_outputs_against_the_oracle():
     assert got[W.PACKET_512x7168.name]["gpu_output_matches"] is False
     assert got[W.TWOSHOT_680x5120_R3.name]["gpu_output_matches"] is False
     assert got[W.WRITE_BCAST_440x5120.name]["gpu_output_matches"] is True
+
+
+# ------------------------------------------------------------------------------
+# Every device buffer a bench row addresses is held by the row.
+#
+# A row's launches, and any HIP graph it captured, address tensors by raw
+# pointer.  If the row does not hold such a tensor, it goes back to torch's
+# cache, and a graph replayed later reads freed memory.  Here stand-ins for
+# torch and for the C library hand out fake device addresses and record every
+# address a launch or a captured graph uses; each must lie inside a tensor the
+# row keeps.
+
+class _FakeTensor:
+    _next = [0x10_0000_0000]
+
+    def __init__(self, nbytes, elem=2):
+        self.nbytes, self.elem = max(int(nbytes), 1), elem
+        self.addr = _FakeTensor._next[0]
+        _FakeTensor._next[0] += (self.nbytes + 0xFFFF) // 0x10000 * 0x10000 + 0x10000
+        self.is_cuda = True
+
+    def data_ptr(self):
+        return self.addr
+
+    def to(self, dev):
+        return self
+
+    def clone(self):
+        return _FakeTensor(self.nbytes, self.elem)
+
+    def view(self, *a):
+        return self
+
+
+def _fake_torch():
+    import types
+
+    def alloc(n, dtype=None, device=None):
+        elem = 1 if dtype == "uint8" else 2
+        return _FakeTensor(n * elem, elem)
+
+    class Graph:
+        def replay(self):
+            pass
+
+    class Capture:
+        def __init__(self, g, stream=None):
+            pass
+
+        def __enter__(self):
+            return self
+
+        def __exit__(self, *a):
+            return False
+
+    cuda = types.SimpleNamespace(synchronize=lambda: None, CUDAGraph=Graph, graph=Capture)
+    return types.SimpleNamespace(device=lambda s: s, int16="int16", uint8="uint8", int32="int32",
+                                 from_numpy=lambda a: _FakeTensor(a.nbytes), empty=alloc,
+                                 zeros=alloc, cuda=cuda)
+
+
+def _fake_ar(touched):
+    import types
+
+    from allreduce_reduction_way_amd import ar as real
+
+    def note(v):
+        if isinstance(v, _FakeTensor):
+            touched.append(v.addr)
+        elif isinstance(v, int) and v >= 0x10_0000_0000:
+            touched.append(v)
+        elif isinstance(v, (list, tuple)):
+            for x in v:
+                note(x)
+
+    def recorder(*args, **kw):
+        note(list(args) + list(kw.values()))
+        return 0
+
+    class Lib:
+        def __getattr__(self, name):
+            return recorder
+
+    lib = Lib()
+    return types.SimpleNamespace(
+        _ptrs=lambda bufs: tuple(b.addr if isinstance(b, _FakeTensor) else b for b in bufs),
+        lib=lambda: lib, ArError=real.ArError, AR_CTRL_BYTES=real.AR_CTRL_BYTES,
+        ar_packet_scratch_bytes=real.ar_packet_scratch_bytes, ar_slice_range=real.ar_slice_range,
+        ar_ll_packets=real.ar_ll_packets, ar_packet_fused_epoch=recorder,
+        ar_packet_fused=recorder, ar_ll_encode=recorder)
+
+
+def test_every_buffer_a_row_addresses_is_kept_by_the_row():
+    import types
+
+    import numpy as np
+
+    from allreduce_reduction_way_amd import workloads as W
+
+    stub_inputs = types.SimpleNamespace(
+        make_inputs=lambda dist, P, n, seed=0: [np.zeros(8, np.uint16) for _ in range(P)])
+    for w in W.ALL:
+        touched = []
+        rows = bench.make_rows([w.name], _fake_torch(), _fake_ar(touched), stub_inputs, W)
+        assert w.name in rows
+        for row in rows.values():
+            step = row.factory(0)
+            for i in range(3):
+                step(i)
+        kept = [t for row in rows.values() for t in row.keep]
+        assert touched, w.name
+        for a in touched:
+            assert any(t.addr <= a < t.addr + t.nbytes for t in kept), (w.name, hex(a))
+
+
+def test_cpu_baseline_parallel_leg_is_bit_identical():
+    import concurrent.futures
+
+    import numpy as np
+
+    from allreduce_reduction_way_amd import inputs as I
+    from oracle import oracle as O
+
+    xs = I.make_inputs("uniform", 8, 10_007, seed=4)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=3) as pool:
+        parts = bench.oracle_write_bcast_parallel(O, xs, pool, 3)
+    assert len(parts) == 3
+    for k in range(8):
+        assert np.array_equal(np.concatenate([p[k] for p in parts]), O.oneshot_sum(xs))
+    cb = bench.cpu_baseline(xs, budget_s=0.02)
+    assert cb["cores"] == bench.host_cores() >= 1
+    assert cb["parallel_equals_single_thread"] is True
+    assert cb["value"] > 0 and cb["single_thread"]["value"] > 0 and cb["cpu_model"]

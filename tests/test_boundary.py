@@ -184,6 +184,9 @@ def test_tuning_validation():
     assert _err(ar.ar_set_reduce_tuning, 3, 0, 0) == ar.AR_EINVAL
     assert _err(ar.ar_set_reduce_tuning, 1, 0, -1) == ar.AR_EINVAL
     assert _err(ar.ar_set_reduce_tuning, 1, 96, 0) == ar.AR_EINVAL
+    assert _err(ar.ar_set_reduce_tuning, 1, 64, 0, 3) == ar.AR_EINVAL
+    assert _err(ar.ar_set_reduce_tuning, 4, 64, 0, 2) == ar.AR_EINVAL   # pipelined: unroll <= 2
+    assert _err(ar.ar_set_reduce_tuning, 1, 64, 0, 16) == ar.AR_EINVAL
     assert _err(ar.ar_set_packet_tuning, -1, 0, 0) == ar.AR_EINVAL
     assert _err(ar.ar_set_packet_tuning, 0, 3, 0) == ar.AR_EINVAL
     assert _err(ar.ar_set_packet_tuning, 0, 0, 2) == ar.AR_EINVAL
@@ -250,3 +253,76 @@ def test_no_kernel_uses_scratch_memory():
     bad = {k: v.get("ScratchSize [bytes/lane]") for k, v in kernels.items()
            if v.get("ScratchSize [bytes/lane]") != "0" or v.get("VGPRs Spill") != "0"}
     assert not bad, bad
+
+
+# ---------------------------------------------- binding: tensor checks (CPU tensors)
+#
+# The binding checks every torch tensor before its address reaches the C ABI;
+# these fail in the checks, so CPU tensors suffice (a tensor that passed them
+# would then be refused for not being on a GPU).
+
+torch = pytest.importorskip("torch")
+
+
+def _elems(n, dtype=None):
+    return torch.zeros(n, dtype=dtype or torch.int16)
+
+
+def test_binding_rejects_short_tensors():
+    n = 64
+    ins = [_elems(n) for _ in range(8)]
+    outs = [_elems(n) for _ in range(8)]
+    with pytest.raises(ValueError, match="bytes"):
+        ar.ar_oneshot_write_bcast(ins, outs[:7] + [_elems(n - 1)], stream=STREAM)
+    with pytest.raises(ValueError, match="bytes"):
+        ar.ar_oneshot_sum(ins, _elems(n), n=n + 1, stream=STREAM)
+    with pytest.raises(ValueError, match="bytes"):
+        ar.ar_reduce_scatter_share(ins, _elems(n // 8 + 1), 3, stream=STREAM)
+    with pytest.raises(ValueError, match="bytes"):
+        ar.ar_ll_encode(ins[0], torch.zeros(16 * ar.ar_ll_packets(n) - 1, dtype=torch.uint8), 1,
+                        stream=STREAM)
+    with pytest.raises(ValueError, match="bytes"):
+        ar.ar_ll_decode(torch.zeros(16 * ar.ar_ll_packets(n), dtype=torch.uint8), _elems(n), 1,
+                        torch.zeros(63, dtype=torch.uint8), stream=STREAM)
+
+
+def test_binding_rejects_short_scratch_and_control_blocks():
+    P, n = 8, 4096
+    ins = [_elems(n) for _ in range(P)]
+    outs = [_elems(n) for _ in range(P)]
+    nb = ar.ar_packet_scratch_bytes(P, n)
+    scr = [torch.zeros(nb, dtype=torch.uint8) for _ in range(P)]
+    ctrl = torch.zeros(ar.AR_CTRL_BYTES, dtype=torch.uint8)
+    with pytest.raises(ValueError, match=r"scratch\[5\]"):
+        ar.ar_packet_fused(ins, scr[:5] + [torch.zeros(nb - 16, dtype=torch.uint8)] + scr[6:], outs,
+                           1, ctrl, stream=STREAM)
+    with pytest.raises(ValueError, match="ctrl"):
+        ar.ar_packet_fused_epoch(ins, scr, outs, ctrl[:32], stream=STREAM)
+
+
+@pytest.mark.parametrize("dtype", ["float32", "float16", "uint8", "int32"])
+def test_binding_rejects_wrong_element_types(dtype):
+    n = 64
+    bad = torch.zeros(n, dtype=getattr(torch, dtype))
+    ins = [_elems(n) for _ in range(8)]
+    with pytest.raises(ValueError, match="bf16 elements"):
+        ar.ar_oneshot_sum(ins[:3] + [bad] + ins[4:], _elems(n), n=n, stream=STREAM)
+    with pytest.raises(ValueError, match="bf16 elements"):
+        ar.ar_twoshot_share(ins, [bad] * 8, 0, n=n, stream=STREAM)
+
+
+def test_binding_rejects_strided_and_expanded_views():
+    n = 64
+    ins = [_elems(n) for _ in range(8)]
+    strided = _elems(2 * n)[::2]
+    expanded = _elems(1).expand(n)
+    for bad in (strided, expanded):
+        with pytest.raises(ValueError, match="contiguous"):
+            ar.ar_oneshot_sum(ins, bad, stream=STREAM)
+        with pytest.raises(ValueError, match="contiguous"):
+            ar.ar_oneshot_write_bcast([bad] + ins[1:], ins, stream=STREAM)
+
+
+def test_binding_needs_n_with_raw_addresses():
+    with pytest.raises(ValueError, match="n is required"):
+        ar.ar_oneshot_sum(_bufs(8), FAKE + (1 << 30), stream=STREAM)
