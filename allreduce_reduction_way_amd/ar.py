@@ -17,12 +17,13 @@ from typing import Sequence
 LIB_PATH = pathlib.Path(__file__).resolve().with_name("libar.so")
 
 AR_MAX_P = 8
-AR_OK, AR_EINVAL, AR_EALIAS, AR_ELAUNCH, AR_ETIMEDOUT = 0, -1, -2, -3, -4
+AR_OK, AR_EINVAL, AR_EALIAS, AR_ELAUNCH, AR_ETIMEDOUT, AR_ENOSPACE = 0, -1, -2, -3, -4, -5
 AR_CTRL_BYTES = 64
+AR_NOALLOC_SCRATCH_BYTES = 64 << 20
 AR_DEFAULT_MAX_SPINS = 1 << 22
 
 _NAMES = {AR_OK: "AR_OK", AR_EINVAL: "AR_EINVAL", AR_EALIAS: "AR_EALIAS",
-          AR_ELAUNCH: "AR_ELAUNCH", AR_ETIMEDOUT: "AR_ETIMEDOUT"}
+          AR_ELAUNCH: "AR_ELAUNCH", AR_ETIMEDOUT: "AR_ETIMEDOUT", AR_ENOSPACE: "AR_ENOSPACE"}
 
 
 class ArError(RuntimeError):
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
             "ar_reduce_scatter_share": (i32, [ar_ptrs, vp, i32, i32, i64, vp]),
             "ar_packet_fused_epoch": (i32, [ar_ptrs, ar_ptrs, ar_ptrs, i32, i32, i32, i64, vp, u64,
                                             vp]),
+            "ar_packet_fused_noalloc": (i32, [ar_ptrs, ar_ptrs, i32, i64, vp, u64, vp]),
             "ar_packet_send": (i32, [ar_ptrs, ar_ptrs, i32, i32, i32, i64, u32, vp]),
             "ar_packet_recv_reduce_send": (i32, [ar_ptrs, i32, i32, i32, i64, u32, vp, u64, vp]),
             "ar_packet_recv": (i32, [ar_ptrs, ar_ptrs, i32, i32, i32, i64, u32, vp, u64, vp]),
@@ -276,6 +278,22 @@ def ar_packet_fused_epoch(inputs: Sequence, scratch: Sequence, outputs: Sequence
     _check(lib().ar_packet_fused_epoch(_ptrs(inputs), _ptrs(scratch), _ptrs(outputs), P, rank_lo,
                                        hi, n, _addr(ctrl), max_spins, _stream(stream)),
            "ar_packet_fused_epoch")
+
+
+def ar_packet_fused_noalloc(inputs: Sequence, outputs: Sequence, status=None,
+                            n: int | None = None, max_spins: int = 0, stream=None) -> None:
+    """The fused packet share of all P ranks with the library's static scratch
+    (nothing is allocated).  `status`: None, or a device int32 that receives
+    AR_OK or AR_ETIMEDOUT when the call completes."""
+    P = len(inputs)
+    if len(outputs) != P:
+        raise ValueError("the packet path needs P inputs and P outputs")
+    n = _n(n, inputs)
+    _packet_buffers(P, n, inputs, None, outputs)
+    _require(status, 4, "status", word=4)
+    _check(lib().ar_packet_fused_noalloc(_ptrs(inputs), _ptrs(outputs), P, n,
+                                         0 if status is None else _addr(status), max_spins,
+                                         _stream(stream)), "ar_packet_fused_noalloc")
 
 
 def ar_packet_send(inputs: Sequence, scratch: Sequence, flag: int, rank_lo: int = 0,

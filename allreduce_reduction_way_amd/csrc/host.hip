@@ -78,6 +78,7 @@ const char *ar_strerror(int code) {
         case AR_EALIAS: return "AR_EALIAS: buffers overlap";
         case AR_ELAUNCH: return "AR_ELAUNCH: kernel launch or device query failed";
         case AR_ETIMEDOUT: return "AR_ETIMEDOUT: a bounded packet wait ran out";
+        case AR_ENOSPACE: return "AR_ENOSPACE: the call needs more than the static scratch";
         default: return "unknown ar status code";
     }
 }

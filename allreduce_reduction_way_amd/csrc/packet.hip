@@ -30,8 +30,18 @@
 // The grid never exceeds the number of workgroups that fit on the device at
 // once, so every workgroup a lane waits on is resident; all waits are bounded
 // and report AR_ETIMEDOUT.
+#include <mutex>
+
 #include "device.h"
 #include "host.h"
+
+// Device memory of ar_packet_fused_noalloc, for callers that cannot allocate:
+// its control block (first 256 bytes) and the P scratch buffers.  Every GPU
+// the library runs on holds its own copy until the process ends; like any
+// object of static storage it starts zeroed.  On the host this name is only
+// a stand-in for the device object: host code never hands it to a kernel, it
+// takes each device's address from hipGetSymbolAddress (noalloc_base).
+static __device__ __align__(256) uint8_t scratch[AR_NOALLOC_SCRATCH_BYTES];
 
 namespace ar {
 namespace {
@@ -132,6 +142,11 @@ struct FusedArgs {
     uint32_t *epoch;   // ar_ctrl.epoch (second word)
     uint32_t *arrivals;  // ar_ctrl.arrivals (third word)
     uint64_t max_spins;
+    // Library-owned control block (static scratch): at the end of an EPOCH
+    // launch the last workgroup copies the status to status_out (if set) and
+    // clears it, so the next call starts from AR_OK.
+    int own_ctrl;
+    int32_t *status_out;
 };
 
 // Elements in slice j (the last slice absorbs the remainder).
@@ -319,9 +334,22 @@ __global__ __launch_bounds__(kThreads) void k_packet_fused(FusedArgs a) {
     if (EPOCH) {
         __syncthreads();
         if (threadIdx.x == 0) {
+            // With a library-owned block the arrival is a release and the last
+            // one an acquire, so a status raised by any lane of any workgroup
+            // is seen by the last workgroup before it reports and clears it.
+            if (a.own_ctrl) __threadfence();
             const uint32_t before = __hip_atomic_fetch_add(a.arrivals, 1u, __ATOMIC_RELAXED,
                                                            __HIP_MEMORY_SCOPE_AGENT);
             if (before == gridDim.x - 1) {
+                if (a.own_ctrl) {
+                    // every workgroup has stopped waiting: nobody reads the status now
+                    __threadfence();
+                    const int32_t st = load_status(a.status);
+                    if (a.status_out)
+                        __hip_atomic_store(a.status_out, st, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(a.status, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
                 __hip_atomic_store(a.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 __hip_atomic_store(a.epoch, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
@@ -475,7 +503,7 @@ int prepare_packet(const ar_ptrs &in, const ar_ptrs &scratch, const ar_ptrs &out
 
 int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const ar_ptrs &out, int P,
                 int rank_lo, int rank_hi, int64_t n, uint32_t flag, void *ctrl, uint64_t max_spins,
-                void *stream) {
+                void *stream, int32_t *status_out = nullptr, bool own_ctrl = false) {
     Kind kind = kind_in;
     if (kind == kFused && g_fused_schedule == 1) kind = kRoles;
     const bool use_in = kind == kFused || kind == kFusedEpoch || kind == kSend || kind == kRoles;
@@ -489,6 +517,8 @@ int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const a
     int rc = prepare_packet(in, scratch, out, use_in, use_out, use_ctrl, P, rank_lo, rank_hi, n,
                             flag, kind != kFusedEpoch, ctrl, max_spins, wpl, &a);
     if (rc != AR_OK || n == 0) return rc;
+    a.own_ctrl = own_ctrl;
+    a.status_out = status_out;
     DeviceInfo dev;
     if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
     FusedKernel fn = wpl == 1 ? pick_p<1>(P, kind) : pick_p<2>(P, kind);
@@ -527,6 +557,34 @@ int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const a
     a.per_rank = (int)B;
     return launch(reinterpret_cast<const void *>(fn), (unsigned)(roles * B * a.nranks), kThreads,
                   a, stream);
+}
+
+// ---- static scratch of ar_packet_fused_noalloc ----------------------------------
+
+constexpr int64_t kNoallocCtrlRegion = 256;  // control block, padded to the array's alignment
+constexpr int64_t kNoallocAlign = 256;       // each rank's scratch buffer starts 256-B aligned
+
+std::mutex g_noalloc_mu;
+uint8_t *g_noalloc_base[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// Device address of the static array on the current device, looked up once
+// per device with that device current; AR_ELAUNCH if the lookup fails.
+int noalloc_base(const DeviceInfo &dev, uint8_t **base) {
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (!g_noalloc_base[dev.device]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr ||
+            !aligned_to(ptr, kNoallocAlign))
+            return AR_ELAUNCH;
+        g_noalloc_base[dev.device] = static_cast<uint8_t *>(ptr);
+    }
+    *base = g_noalloc_base[dev.device];
+    return AR_OK;
+}
+
+// Bytes of one rank's scratch buffer inside the static array.
+int64_t noalloc_rank_stride(int P, int64_t n) {
+    return round_up(ar_packet_scratch_bytes(P, n), kNoallocAlign);
 }
 
 }  // namespace
@@ -603,6 +661,35 @@ int ar_packet_fused_epoch(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int r
                           int rank_hi, int64_t n, void *ctrl, uint64_t max_spins, void *stream) {
     return packet_call(kFusedEpoch, in, scratch, out, P, rank_lo, rank_hi, n, 0, ctrl, max_spins,
                        stream);
+}
+
+int ar_packet_fused_noalloc(ar_ptrs in, ar_ptrs out, int P, int64_t n, int32_t *d_status,
+                            uint64_t max_spins, void *stream) {
+    // host-only checks first: nothing touches the GPU for a call that cannot run
+    if (!valid_P(P) || n < 0) return AR_EINVAL;
+    if (d_status && !aligned_to(d_status, 4)) return AR_EINVAL;
+    for (int p = 0; p < P; ++p) {
+        if (!in.p[p] || !aligned_to(in.p[p], 2)) return AR_EINVAL;
+        if (!out.p[p] || !aligned_to(out.p[p], 2)) return AR_EINVAL;
+    }
+    const int64_t stride = noalloc_rank_stride(P, n);
+    if (kNoallocCtrlRegion + (int64_t)P * stride > (int64_t)AR_NOALLOC_SCRATCH_BYTES)
+        return AR_ENOSPACE;
+    if (d_status) {
+        const Span ss = span_of(d_status, 0, 4, 1);
+        for (int p = 0; p < P; ++p)
+            if (overlap(ss, span_of(in.p[p], 0, n, 2)) || overlap(ss, span_of(out.p[p], 0, n, 2)))
+                return AR_EALIAS;
+    }
+    if (n == 0) return AR_OK;
+    DeviceInfo dev;
+    if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
+    uint8_t *base = nullptr;
+    if (noalloc_base(dev, &base) != AR_OK) return AR_ELAUNCH;
+    ar_ptrs bufs = {};
+    for (int p = 0; p < P; ++p) bufs.p[p] = base + kNoallocCtrlRegion + (int64_t)p * stride;
+    return packet_call(kFusedEpoch, in, bufs, out, P, 0, P, n, 0, base, max_spins, stream,
+                       d_status, true);
 }
 
 int ar_packet_send(ar_ptrs in, ar_ptrs scratch, int P, int rank_lo, int rank_hi, int64_t n,

@@ -54,7 +54,8 @@ enum ar_status {
     AR_EINVAL = -1,    /* bad argument: P, n, rank, flag, null or misaligned pointer */
     AR_EALIAS = -2,    /* buffers overlap where the call forbids it */
     AR_ELAUNCH = -3,   /* the HIP launch (or a device query it needs) failed */
-    AR_ETIMEDOUT = -4  /* device side: a bounded wait for a packet ran out */
+    AR_ETIMEDOUT = -4, /* device side: a bounded wait for a packet ran out */
+    AR_ENOSPACE = -5   /* the call needs more than the library's static scratch */
 };
 
 /*
@@ -218,6 +219,36 @@ int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo
  * ------------------------------------------------------------------------- */
 int ar_packet_fused_epoch(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo,
                           int rank_hi, int64_t n, void *ctrl, uint64_t max_spins, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * ar_packet_fused_noalloc -- ar_packet_fused_epoch for all P ranks, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the control block
+ * and the P scratch buffers live in one static device array of the library,
+ * AR_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  The call
+ * allocates nothing; the caller passes only inputs, outputs and an optional
+ * status word.
+ *   in, out   P inputs / P outputs of n bf16, as for ar_packet_fused (no
+ *             overlaps: AR_EALIAS).  Every rank 0..P-1 runs in the launch.
+ *   d_status  NULL, or a 4-byte aligned device int32 that receives AR_OK or
+ *             AR_ETIMEDOUT when the call completes (written on the stream).
+ *   max_spins as for ar_packet_fused.
+ * Size limit: 256 + P * round_up(ar_packet_scratch_bytes(P, n), 256) must not
+ * exceed AR_NOALLOC_SCRATCH_BYTES, otherwise AR_ENOSPACE is returned before
+ * anything touches the GPU (at P = 8: n up to 1,047,676 elements).
+ * The array starts zeroed; the flag of a call is the array's epoch + 1, so it
+ * rises with every call on the GPU whatever P and n are, and a packet left by
+ * an earlier call never matches.  Each call leaves the array's status word
+ * cleared for the next one.  All calls on one GPU share its array: two calls
+ * in flight at once on one GPU (two streams, two host threads) race and give
+ * undefined results; calls ordered on one stream are safe.  The first call on
+ * a device looks up the array's address there (hipGetSymbolAddress) and
+ * returns AR_ELAUNCH if that fails.  Wrap-around after 2^32 - 1 calls is not
+ * supported.
+ * ------------------------------------------------------------------------- */
+#define AR_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int ar_packet_fused_noalloc(ar_ptrs in, ar_ptrs out, int P, int64_t n, int32_t *d_status,
+                            uint64_t max_spins, void *stream);
 
 /* ---------------------------------------------------------------------------
  * The three-operation packet decomposition that the fused kernel replaces

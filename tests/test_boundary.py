@@ -75,7 +75,7 @@ def test_ll_packets():
 
 def test_strerror_names_every_code():
     for code, name in [(0, "AR_OK"), (-1, "AR_EINVAL"), (-2, "AR_EALIAS"), (-3, "AR_ELAUNCH"),
-                       (-4, "AR_ETIMEDOUT")]:
+                       (-4, "AR_ETIMEDOUT"), (-5, "AR_ENOSPACE")]:
         assert ar.ar_strerror(code).startswith(name)
 
 
@@ -255,6 +255,44 @@ def test_no_kernel_uses_scratch_memory():
     assert not bad, bad
 
 
+def test_noalloc_host_checks_come_before_the_gpu():
+    """ar_packet_fused_noalloc rejects bad arguments and sizes beyond its static
+    scratch on the host; n == 0 is a no-op that never touches the device."""
+    P = 8
+    ins, outs = _bufs(P), _bufs(P, base=FAKE + (1 << 30))
+    st = FAKE + (3 << 30)
+
+    def fits(P, n):
+        per = -(-O.packet_scratch_bytes(P, n) // 256) * 256
+        return 256 + P * per <= ar.AR_NOALLOC_SCRATCH_BYTES
+
+    # the largest n that fits, found from the oracle's scratch size rule
+    lo, hi = 0, 1 << 24
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        lo, hi = (mid, hi) if fits(P, mid) else (lo, mid - 1)
+    assert lo == 1_047_676                     # the figure include/ar.h states for P = 8
+    assert _err(ar.ar_packet_fused_noalloc, ins, outs, st, n=lo + 1,
+                stream=STREAM) == ar.AR_ENOSPACE
+    assert _err(ar.ar_packet_fused_noalloc, ins, outs, st, n=1 << 30,
+                stream=STREAM) == ar.AR_ENOSPACE
+    assert _err(ar.ar_packet_fused_noalloc, ins, outs, st, n=-1, stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_packet_fused_noalloc, ins, outs, st + 2, n=16,
+                stream=STREAM) == ar.AR_EINVAL   # status not 4-byte aligned
+    assert _err(ar.ar_packet_fused_noalloc, ins[:7] + [0], outs, st, n=16,
+                stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_packet_fused_noalloc, ins, outs[:7] + [outs[7] + 1], st, n=16,
+                stream=STREAM) == ar.AR_EINVAL
+    assert _err(ar.ar_packet_fused_noalloc, ins, outs, outs[2] + 8, n=16,
+                stream=STREAM) == ar.AR_EALIAS   # status inside an output
+    L = ar.lib()
+    for bad_P in (1, 9):
+        assert L.ar_packet_fused_noalloc(ar._ptrs(ins), ar._ptrs(outs), bad_P, 16, st, 0,
+                                         STREAM) == ar.AR_EINVAL
+    ar.ar_packet_fused_noalloc(ins, outs, st, n=0, stream=STREAM)        # no-op
+    ar.ar_packet_fused_noalloc(ins, outs, None, n=0, stream=STREAM)
+
+
 # ---------------------------------------------- binding: tensor checks (CPU tensors)
 #
 # The binding checks every torch tensor before its address reaches the C ABI;
@@ -298,6 +336,10 @@ def test_binding_rejects_short_scratch_and_control_blocks():
                            1, ctrl, stream=STREAM)
     with pytest.raises(ValueError, match="ctrl"):
         ar.ar_packet_fused_epoch(ins, scr, outs, ctrl[:32], stream=STREAM)
+    with pytest.raises(ValueError, match="status"):
+        ar.ar_packet_fused_noalloc(ins, outs, torch.zeros(1, dtype=torch.int64), stream=STREAM)
+    with pytest.raises(ValueError, match="status"):
+        ar.ar_packet_fused_noalloc(ins, outs, torch.zeros(0, dtype=torch.int32), stream=STREAM)
 
 
 @pytest.mark.parametrize("dtype", ["float32", "float16", "uint8", "int32"])
