@@ -15,7 +15,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 LIB = PKG / "libar.so"
 RESOURCES = PKG / "libar.resources.txt"   # per-kernel register/scratch report of the last build
-SOURCES = ["host.hip", "reduce.hip", "packet.hip"]
+SOURCES = ["host.hip", "reduce.hip", "packet.hip", "probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

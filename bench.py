@@ -29,6 +29,10 @@ evicts L2 and the 256 MB MALL ("cold"; the event pair itself adds about
 mean launch duration over the timed region (one launch per step; an event
 pair around each single launch is also reported, it adds the events' own
 overhead);
+`ceilings` gives what the device delivers for the headline's 72 MB at that
+size with the data in HBM: probe kernels of the library that read all 16
+buffers, write all 16, or copy the 8 inputs into the 8 outputs, with the
+reduce kernel's own accesses and no arithmetic, over rotating buffer sets.
 `traffic` is the FETCH_SIZE + WRITE_SIZE bytes per launch recorded by
 rocprofv3 in profiles/, scaled by the same counters' reading for a plain copy
 of known size, or null when the kernels changed after the counters were
@@ -40,6 +44,7 @@ each row's own inputs for about 1.5 s each, single-threaded.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only-headline      (profiling runs: the headline only)
        python bench.py --copy-probe         (counter calibration: a plain copy)
+       python bench.py --ceilings           (profiling runs: same-size ceilings, cold)
 """
 from __future__ import annotations
 
@@ -410,6 +415,89 @@ class RotatingSets:
         return all(torch.equal(o, first) for s_ in self.outs for o in s_)
 
 
+PROBE_KINDS = {0: "read_only", 1: "write_only", 2: "copy"}
+# (threads, unroll) launch shapes tried for each probe kernel, one pass each
+PROBE_SHAPES = [(64, 1), (64, 2), (64, 4), (128, 1), (256, 1), (256, 2)]
+
+
+def probe_sets(torch, P, n, sets):
+    """`sets` sets of P inputs + P outputs of n bf16 for the probe kernels."""
+    return [([torch.ones(n, dtype=torch.int16, device="cuda:0") for _ in range(P)],
+             [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(P)])
+            for _ in range(sets)]
+
+
+def time_ceilings(torch, ar, stream, P, n, steps, sets=8):
+    """What the device delivers for the headline's bytes at its size with the
+    data in HBM: the probe kernels (read all 2P buffers, write all 2P, copy P
+    into P: 2 x P x n x 2 B each, the reduce kernel's accesses) over `sets`
+    rotating buffer sets, back to back; the best launch shape per kind."""
+    P_, s = ar._ptrs, int(stream.cuda_stream)
+    bufs = probe_sets(torch, P, n, sets)
+    nbytes = 2 * P * n * 2
+    out = {}
+    for kind, name in PROBE_KINDS.items():
+        best = None
+        for th, u in PROBE_SHAPES:
+            if kind == 0 and u > 2:
+                continue
+            calls = [_raw(ar, "ar_probe_traffic", kind, P_(i), P_(o), P, n, th, u, 0, s)
+                     for i, o in bufs]
+            ms, _ = time_streamed(torch, stream, lambda i: calls[i % sets](), steps, 2 * sets)
+            if best is None or ms < best[0]:
+                best = (ms, th, u)
+        us = best[0] * 1e3
+        out[name] = {"us": round(us, 3), "gbs": round(gbs(nbytes, us), 1),
+                     "frac": round(gbs(nbytes, us) / HBM_PEAK_GBS, 4),
+                     "threads": best[1], "unroll": best[2]}
+    del bufs
+    return out
+
+
+def ceilings_mode(torch, ar, I, W, stream, reps=12):
+    """--ceilings: every probe shape, the library's own call and an empty
+    kernel, each launched `reps` times right after a 512 MiB read-only scrub
+    (run under rocprofv3 --kernel-trace: the trace gives each launch's cold
+    duration; `order` lists the launches of interest in dispatch order), at
+    the write-mode headline's size and at the two-shot rank-3 slice's size
+    (435,200 elements: the same kernel and launch shape as
+    ar_twoshot_share(rank 3) of 680x5120 x 8, as a write-mode call of that
+    length).  Also the headline-size ceilings over rotating sets."""
+    P_, s = ar._ptrs, int(stream.cuda_stream)
+    P = 8
+    scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
+    order = []
+    cases = [("write_bcast_440x5120_p8", W.WRITE_BCAST_440x5120.n),
+             ("twoshot_680x5120_p8_rank3_slice", 435200)]
+    for label, n in cases:
+        bufs = probe_sets(torch, P, n, 2)
+        xs = [torch.from_numpy(x.view("int16")).to("cuda:0")
+              for x in I.make_inputs("uniform", P, n, seed=0)]
+        outs = [torch.empty(n, dtype=torch.int16, device="cuda:0") for _ in range(P)]
+        launches = [("empty kernel", _raw(ar, "ar_noop", s)),
+                    ("write-mode call (automatic shape)",
+                     _raw(ar, "ar_oneshot_write_bcast", P_(xs), P_(outs), P, n, s))]
+        for kind, name in PROBE_KINDS.items():
+            for th, u in PROBE_SHAPES:
+                if kind == 0 and u > 2:
+                    continue
+                launches.append((f"{name} {th} lanes x {u}",
+                                 _raw(ar, "ar_probe_traffic", kind, P_(bufs[0][0]), P_(bufs[0][1]),
+                                      P, n, th, u, 0, s)))
+        torch.cuda.synchronize()
+        for what, call in launches:
+            with torch.cuda.stream(stream):
+                for _ in range(reps):
+                    scrub.view(torch.int32).amax()
+                    call()
+                    order.append([label, what])
+            torch.cuda.synchronize()
+        del bufs, xs, outs
+    rot = time_ceilings(torch, ar, stream, P, W.WRITE_BCAST_440x5120.n, 200)
+    return {"order": order, "rotating_ceilings_440x5120_p8": rot,
+            "bytes": {c[0]: 2 * P * c[1] * 2 for c in cases}}
+
+
 def time_copy_reference(torch, stream, nbytes, steps, sets=8):
     """A plain device copy (torch's copy_, i.e. the runtime's own copy kernel)
     of `nbytes`, which moves the same bytes as the headline when nbytes is its
@@ -629,6 +717,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--rows", default="", help="comma-separated workload names (default: all)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="profiling: probe kernels and the library's call, each right after a "
+                         "512 MiB scrub (cold), plus the rotating-set ceilings")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cold-calls", type=int, default=20)
     ap.add_argument("--per-call", type=int, default=50, help="event-pair calls per row")
@@ -658,6 +749,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copy probe: {args.steps} copies of {COPY_PROBE_BYTES} bytes")
+        return
+
+    if args.ceilings:
+        print(json.dumps(ceilings_mode(torch, ar, I, W, stream)), flush=True)
         return
 
     headline = W.WRITE_BCAST_440x5120
@@ -733,6 +828,13 @@ def main():
                     "note": "torch copy_ of the headline's 36 MB input volume into a second "
                             "buffer: a plain kernel moving the same 72 MB"})
         result["copy_reference"] = ref
+        # what the device delivers for the same bytes at this size, data in HBM
+        log("same-size ceilings (probe kernels over rotating sets)")
+        result["ceilings"] = time_ceilings(torch, ar, stream, headline.P, headline.n,
+                                           min(max(args.steps, 100), 400))
+        result["ceilings"]["note"] = ("the headline's 72,089,600 B read-only, write-only and "
+                                      "copied (no arithmetic) with the reduce kernel's "
+                                      "accesses, over 8 rotating sets: data in HBM")
 
     if not args.only_headline:
         out_rows = {}

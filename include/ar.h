@@ -292,6 +292,19 @@ const char *ar_strerror(int code);
  * ------------------------------------------------------------------------- */
 int ar_noop(void *stream);
 
+/* Measurement helper: the traffic of a write-mode call without the reduction,
+ * to measure what the device delivers for the same bytes at the same size.
+ * kind 0 reads all 2P buffers (in.p[0..P-1] and out.p[0..P-1]), kind 1 writes
+ * all 2P of them (contents become meaningless), kind 2 copies in.p[p] into
+ * out.p[p].  The accesses are those of the reduce kernels: 16-byte loads,
+ * 16-byte stores with the same cache policy, `unroll` vectors in flight per
+ * lane (1 or 2 for kind 0; 1, 2 or 4 otherwise), `threads` in {64, 128, 256}
+ * lanes per workgroup, `blocks` workgroups at most (0: one pass, one vector
+ * per lane per unroll step).  P is 4 or 8; n elements per buffer, a multiple
+ * of 8, at most 2^29; every buffer 16-byte aligned and none overlapping. */
+int ar_probe_traffic(int kind, ar_ptrs in, ar_ptrs out, int P, int64_t n, int threads, int unroll,
+                     int blocks, void *stream);
+
 /* Benchmark-only launch-shape overrides (process-global, not thread-safe).
  * ar_set_reduce_tuning: unroll (vectors in flight per lane) in {0 = automatic,
  * 1, 2, 4}, workgroup size in {0 = automatic, 64, 128, 256}, a cap on

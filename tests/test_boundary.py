@@ -368,3 +368,21 @@ def test_binding_rejects_strided_and_expanded_views():
 def test_binding_needs_n_with_raw_addresses():
     with pytest.raises(ValueError, match="n is required"):
         ar.ar_oneshot_sum(_bufs(8), FAKE + (1 << 30), stream=STREAM)
+
+
+def test_probe_traffic_validation():
+    ins, outs = _bufs(8), _bufs(8, base=FAKE + (1 << 30))
+    L = ar.lib()
+    P_ = ar._ptrs
+    ok = (P_(ins), P_(outs), 8, 4096, 64, 1, 0, STREAM)
+    assert L.ar_probe_traffic(3, *ok) == ar.AR_EINVAL                              # kind
+    assert L.ar_probe_traffic(0, P_(ins), P_(outs), 8, 4096, 64, 4, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 3, 4096, 64, 1, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 8, 4095, 64, 1, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 8, 4096, 96, 1, 0, STREAM) == ar.AR_EINVAL
+    bad = list(outs)
+    bad[3] = ins[5] + 64                                                          # overlap
+    assert L.ar_probe_traffic(2, P_(ins), P_(bad), 8, 4096, 64, 1, 0, STREAM) == ar.AR_EALIAS
+    bad = list(ins)
+    bad[1] = ins[1] + 8                                                           # not 16-B
+    assert L.ar_probe_traffic(2, P_(bad), P_(outs), 8, 4096, 64, 1, 0, STREAM) == ar.AR_EINVAL

@@ -352,3 +352,54 @@ def test_ll_encode_from_two_byte_aligned_source(n):
     ar.ar_ll_encode(src.view, pk, 77)
     torch.cuda.synchronize()
     assert np.array_equal(pk.cpu().numpy().view(np.uint32), O.ll_encode(y, 77))
+
+
+@pytest.mark.parametrize("in_shift,out_shift", [(0, 0), (2, 0), (0, 2), (1, 3), (2, 2)])
+def test_packet_every_path_and_alignment(in_shift, out_shift):
+    """The fused kernel, its epoch variant and the three-launch decomposition
+    with buffers 8-, 4- and 2-byte aligned (element accesses fall back from
+    pairs to single elements): outputs and scratch images bit-exact, call
+    after call, the paths interleaved on one scratch set."""
+    P, n = 8, 8192 * 5 + 13
+    scratch = _scratch(P, n)
+    images = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    ctrl = ctrl_block()
+    for f, path in ((1, "fused"), (2, "three-op"), (3, "fused")):
+        xs = I.make_inputs("uniform", P, n, seed=90 + f + in_shift)
+        ins = [Guarded(n, shift=in_shift, init=x) for x in xs]
+        outs = [Guarded(n, shift=out_shift) for _ in range(P)]
+        announce(f"packet {path} flag={f} shifts in={in_shift} out={out_shift}")
+        iv, ov = [g.view for g in ins], [o.view for o in outs]
+        if path == "fused":
+            ar.ar_packet_fused(iv, scratch, ov, f, ctrl)
+        else:
+            ar.ar_packet_send(iv, scratch, f)
+            ar.ar_packet_recv_reduce_send(scratch, n, f, ctrl)
+            ar.ar_packet_recv(scratch, ov, f, ctrl)
+        torch.cuda.synchronize()
+        assert ctrl_status(ctrl) == 0
+        want, images = O.packet_fused(xs, f, images)
+        for r in range(P):
+            assert np.array_equal(outs[r].host(), want[r]), (f, r)
+            assert outs[r].guards_intact()
+        got = _images(scratch)
+        for r in range(P):
+            assert np.array_equal(got[r], images[r]), (f, r)
+    # the device-epoch variant on a fresh scratch set (flag 1, then 2)
+    scratch = _scratch(P, n)
+    images = [np.zeros(O.packet_scratch_bytes(P, n), np.uint8) for _ in range(P)]
+    ectrl = ctrl_block()
+    for f in (1, 2):
+        xs = I.make_inputs("uniform", P, n, seed=95 + f)
+        outs = [Guarded(n, shift=out_shift) for _ in range(P)]
+        ins = [Guarded(n, shift=in_shift, init=x) for x in xs]
+        announce(f"packet epoch call {f} shifts in={in_shift} out={out_shift}")
+        ar.ar_packet_fused_epoch([g.view for g in ins], scratch, [o.view for o in outs], ectrl)
+        torch.cuda.synchronize()
+        assert ctrl_status(ectrl) == 0
+        want, images = O.packet_fused(xs, f, images)
+        for r in range(P):
+            assert np.array_equal(outs[r].host(), want[r]), (f, r)
+        got = _images(scratch)
+        for r in range(P):
+            assert np.array_equal(got[r], images[r]), (f, r)
