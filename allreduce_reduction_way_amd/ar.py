@@ -70,7 +70,7 @@ def lib() -> ctypes.CDLL:
             "ar_packet_scratch_bytes": (i64, [i32, i64]),
             "ar_strerror": (ctypes.c_char_p, [i32]),
             "ar_noop": (i32, [vp]),
-            "ar_probe_traffic": (i32, [i32, ar_ptrs, ar_ptrs, i32, i64, i32, i32, i32, vp]),
+            "ar_probe_traffic": (i32, [i32, ar_ptrs, ar_ptrs, i32, i64, i32, i32, i32, i32, vp]),
             "ar_set_reduce_tuning": (i32, [i32, i32, i32, i32]),
             "ar_set_packet_tuning": (i32, [i32, i32, i32]),
         }
@@ -361,7 +361,7 @@ def ar_noop(stream=None) -> None:
 
 
 def ar_probe_traffic(kind: int, inputs: Sequence, outputs: Sequence, threads: int = 64,
-                     unroll: int = 1, blocks: int = 0, n: int | None = None,
+                     unroll: int = 1, blocks: int = 0, policy: int = 0, n: int | None = None,
                      stream=None) -> None:
     """Measurement helper: read (kind 0), write (1) or copy (2) the 2P
     buffers of a write-mode call with the reduce kernels' accesses."""
@@ -371,7 +371,7 @@ def ar_probe_traffic(kind: int, inputs: Sequence, outputs: Sequence, threads: in
     _require_all(inputs, _ELEM_BYTES * n, "inputs", elems=True)
     _require_all(outputs, _ELEM_BYTES * n, "outputs", elems=True)
     _check(lib().ar_probe_traffic(kind, _ptrs(inputs), _ptrs(outputs), len(inputs), n, threads,
-                                  unroll, blocks, _stream(stream)), "ar_probe_traffic")
+                                  unroll, blocks, policy, _stream(stream)), "ar_probe_traffic")
 
 
 def ar_set_reduce_tuning(unroll: int = 0, threads: int = 0, max_blocks: int = 0,

@@ -85,14 +85,17 @@ __device__ __forceinline__ u32x4 load_vec(const void *base, int64_t elem) {
     return *p;
 }
 
-// Results are written once and never read back by the kernel.  They are
-// stored with cache policy SC1 | NT (operand 18: SC1 = 16, NT = 2): device
-// scope, so each store writes through this XCD's L2 instead of waiting there
-// for the end-of-kernel write-back, plus the streaming hint.  Measured on
-// MI355X against the plain non-temporal store (NT alone): write-mode
+// Results are written once and never read back by the kernel.  WT = true
+// stores them with cache policy SC1 | NT (operand 18: SC1 = 16, NT = 2):
+// device scope, so each store writes through this XCD's L2 instead of
+// waiting there for the end-of-kernel write-back, plus the streaming hint.
+// Measured on MI355X against NT alone, for the grid-stride shapes: write-mode
 // 440x5120 x 8 9.58 instead of 10.18 us back to back (MALL-resident) and
 // 15.57 instead of 15.72 us from HBM; two-shot rank 3 of 680x5120 x 8 3.20
-// instead of 3.35 us.  (SC1 without NT: 9.30 us warm but 17.4 us from HBM.)
+// instead of 3.35 us.  (SC1 without NT: 9.30 us warm but 17.4 us from HBM;
+// no policy bits: 17.7 against 14.4 us from HBM.)  WT = false stores with NT
+// alone: the one-pass kernel that issues four vectors per lane per input
+// before storing any runs better without the write-through (below).
 //
 // The store goes through a buffer resource so the policy can be chosen:
 // `base` must be the same for every lane of the wavefront (a kernel argument)
@@ -106,10 +109,11 @@ constexpr uint32_t kStoreRangeBytes = 0x7FFFFFFFu;
 constexpr uint32_t kDroppedStoreOffset = 0x80000000u;
 static_assert(kDroppedStoreOffset >= kStoreRangeBytes, "a dropped store must be out of range");
 
+template <bool WT = true>
 __device__ __forceinline__ void store_vec(void *base, uint32_t byte_off, u32x4 v) {
     const __amdgpu_buffer_rsrc_t r =
         __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kStoreRangeBytes, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 18);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, WT ? 18 : 2);
 }
 
 // ---- packet words -----------------------------------------------------------

@@ -5,11 +5,12 @@
 // Three kernels over 2P buffers of n bf16 (the P inputs and P outputs of a
 // write-mode call): read every one of them (read-only), write every one of
 // them (write-only), or copy input p to output p (the reduce kernel's bytes
-// with no arithmetic).  They use the reduce kernel's accesses: 16-byte plain
-// loads, 16-byte buffer stores with the same cache policy (store_vec), U
-// vectors in flight per lane, grid stride.  Results are meaningless by
-// design (the read-only kernel keeps an xor of what it read only so that the
-// loads cannot be dropped).
+// with no arithmetic).  They use the reduce kernels' accesses: 16-byte
+// loads, 16-byte buffer stores (store_vec), U vectors in flight per lane,
+// grid stride, with either cache policy the reduce kernels take (NT = false:
+// plain loads, write-through streaming stores; NT = true: non-temporal loads
+// and stores).  Results are meaningless by design (the read-only kernel keeps
+// an xor of what it read only so that the loads cannot be dropped).
 #include "device.h"
 #include "host.h"
 
@@ -23,7 +24,7 @@ struct ProbeArgs {
     uint32_t *sink;  // read-only: one word written only if an impossible xor comes up
 };
 
-template <int P, int U>
+template <int P, int U, bool NT>
 __global__ __launch_bounds__(kThreads) void k_probe_read(ProbeArgs a) {
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -36,8 +37,8 @@ __global__ __launch_bounds__(kThreads) void k_probe_read(ProbeArgs a) {
             if (v < a.nvec) {
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
-                    x[u][p] = load_vec<false>(a.in.p[p], 8 * v);
-                    x[u][P + p] = load_vec<false>(a.out.p[p], 8 * v);
+                    x[u][p] = load_vec<NT>(a.in.p[p], 8 * v);
+                    x[u][P + p] = load_vec<NT>(a.out.p[p], 8 * v);
                 }
             }
         }
@@ -53,7 +54,7 @@ __global__ __launch_bounds__(kThreads) void k_probe_read(ProbeArgs a) {
     if (acc == 0x9E3779B9u && a.sink) a.sink[0] = acc;
 }
 
-template <int P, int U>
+template <int P, int U, bool NT>
 __global__ __launch_bounds__(kThreads) void k_probe_write(ProbeArgs a) {
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -66,15 +67,15 @@ __global__ __launch_bounds__(kThreads) void k_probe_write(ProbeArgs a) {
                 const uint32_t off = (uint32_t)(16 * v);
 #pragma unroll
                 for (int p = 0; p < P; ++p) {
-                    store_vec(a.in.p[p], off, x);
-                    store_vec(a.out.p[p], off, x);
+                    store_vec<!NT>(a.in.p[p], off, x);
+                    store_vec<!NT>(a.out.p[p], off, x);
                 }
             }
         }
     }
 }
 
-template <int P, int U>
+template <int P, int U, bool NT>
 __global__ __launch_bounds__(kThreads) void k_probe_copy(ProbeArgs a) {
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(kThreads) void k_probe_copy(ProbeArgs a) {
             const int64_t v = v0 + u * nth;
             if (v < a.nvec) {
 #pragma unroll
-                for (int p = 0; p < P; ++p) x[u][p] = load_vec<false>(a.in.p[p], 8 * v);
+                for (int p = 0; p < P; ++p) x[u][p] = load_vec<NT>(a.in.p[p], 8 * v);
             }
         }
 #pragma unroll
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads) void k_probe_copy(ProbeArgs a) {
             const int64_t v = v0 + u * nth;
             if (v < a.nvec) {
 #pragma unroll
-                for (int p = 0; p < P; ++p) store_vec(a.out.p[p], (uint32_t)(16 * v), x[u][p]);
+                for (int p = 0; p < P; ++p) store_vec<!NT>(a.out.p[p], (uint32_t)(16 * v), x[u][p]);
             }
         }
     }
@@ -101,11 +102,13 @@ __global__ __launch_bounds__(kThreads) void k_probe_copy(ProbeArgs a) {
 
 typedef void (*ProbeKernel)(ProbeArgs);
 
-template <int P>
+template <int P, bool NT>
 ProbeKernel pick_probe(int kind, int U) {
-    if (kind == 0) return U == 1 ? k_probe_read<P, 1> : k_probe_read<P, 2>;
-    if (kind == 1) return U == 1 ? k_probe_write<P, 1> : (U == 2 ? k_probe_write<P, 2> : k_probe_write<P, 4>);
-    return U == 1 ? k_probe_copy<P, 1> : (U == 2 ? k_probe_copy<P, 2> : k_probe_copy<P, 4>);
+    if (kind == 0) return U == 1 ? k_probe_read<P, 1, NT> : k_probe_read<P, 2, NT>;
+    if (kind == 1)
+        return U == 1 ? k_probe_write<P, 1, NT>
+                      : (U == 2 ? k_probe_write<P, 2, NT> : k_probe_write<P, 4, NT>);
+    return U == 1 ? k_probe_copy<P, 1, NT> : (U == 2 ? k_probe_copy<P, 2, NT> : k_probe_copy<P, 4, NT>);
 }
 
 // The bulk of one probe launch addresses at most this many elements per
@@ -121,8 +124,9 @@ using namespace ar;
 extern "C" {
 
 int ar_probe_traffic(int kind, ar_ptrs in, ar_ptrs out, int P, int64_t n, int threads, int unroll,
-                     int blocks, void *stream) {
+                     int blocks, int policy, void *stream) {
     if (!(kind == 0 || kind == 1 || kind == 2) || !(P == 4 || P == 8) || n <= 0 || n % 8 != 0 ||
+        !(policy == 0 || policy == 1) ||
         n > kProbeMaxElems || !(threads == 64 || threads == 128 || threads == 256) ||
         !(unroll == 1 || unroll == 2 || (unroll == 4 && kind != 0)) || blocks < 0)
         return AR_EINVAL;
@@ -142,7 +146,8 @@ int ar_probe_traffic(int kind, ar_ptrs in, ar_ptrs out, int P, int64_t n, int th
     a.nvec = n / 8;
     int64_t grid = (a.nvec + (int64_t)threads * unroll - 1) / ((int64_t)threads * unroll);
     if (blocks > 0 && grid > blocks) grid = blocks;
-    ProbeKernel fn = P == 4 ? pick_probe<4>(kind, unroll) : pick_probe<8>(kind, unroll);
+    ProbeKernel fn = policy ? (P == 4 ? pick_probe<4, true>(kind, unroll) : pick_probe<8, true>(kind, unroll))
+                            : (P == 4 ? pick_probe<4, false>(kind, unroll) : pick_probe<8, false>(kind, unroll));
     return launch(reinterpret_cast<const void *>(fn), (unsigned)grid, (unsigned)threads, a, stream);
 }
 

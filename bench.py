@@ -416,8 +416,11 @@ class RotatingSets:
 
 
 PROBE_KINDS = {0: "read_only", 1: "write_only", 2: "copy"}
-# (threads, unroll) launch shapes tried for each probe kernel, one pass each
-PROBE_SHAPES = [(64, 1), (64, 2), (64, 4), (128, 1), (256, 1), (256, 2)]
+# (threads, unroll, policy) launch shapes and cache policies tried for each
+# probe kernel, one pass each (policy 0: plain loads, write-through stores;
+# 1: non-temporal loads and stores -- the two the reduce kernels use)
+PROBE_SHAPES = [(64, 1, 0), (64, 2, 0), (64, 4, 0), (128, 1, 0), (256, 1, 0), (256, 2, 0),
+                (64, 1, 1), (64, 2, 1), (64, 4, 1), (256, 1, 1)]
 
 
 def probe_sets(torch, P, n, sets):
@@ -438,18 +441,19 @@ def time_ceilings(torch, ar, stream, P, n, steps, sets=8):
     out = {}
     for kind, name in PROBE_KINDS.items():
         best = None
-        for th, u in PROBE_SHAPES:
+        for th, u, pol in PROBE_SHAPES:
             if kind == 0 and u > 2:
                 continue
-            calls = [_raw(ar, "ar_probe_traffic", kind, P_(i), P_(o), P, n, th, u, 0, s)
+            calls = [_raw(ar, "ar_probe_traffic", kind, P_(i), P_(o), P, n, th, u, 0, pol, s)
                      for i, o in bufs]
             ms, _ = time_streamed(torch, stream, lambda i: calls[i % sets](), steps, 2 * sets)
             if best is None or ms < best[0]:
-                best = (ms, th, u)
+                best = (ms, th, u, pol)
         us = best[0] * 1e3
         out[name] = {"us": round(us, 3), "gbs": round(gbs(nbytes, us), 1),
                      "frac": round(gbs(nbytes, us) / HBM_PEAK_GBS, 4),
-                     "threads": best[1], "unroll": best[2]}
+                     "threads": best[1], "unroll": best[2],
+                     "policy": "non-temporal" if best[3] else "plain loads, write-through stores"}
     del bufs
     return out
 
@@ -478,12 +482,12 @@ def ceilings_mode(torch, ar, I, W, stream, reps=12):
                     ("write-mode call (automatic shape)",
                      _raw(ar, "ar_oneshot_write_bcast", P_(xs), P_(outs), P, n, s))]
         for kind, name in PROBE_KINDS.items():
-            for th, u in PROBE_SHAPES:
+            for th, u, pol in PROBE_SHAPES:
                 if kind == 0 and u > 2:
                     continue
-                launches.append((f"{name} {th} lanes x {u}",
+                launches.append((f"{name} {th} lanes x {u}{' NT' if pol else ''}",
                                  _raw(ar, "ar_probe_traffic", kind, P_(bufs[0][0]), P_(bufs[0][1]),
-                                      P, n, th, u, 0, s)))
+                                      P, n, th, u, 0, pol, s)))
         torch.cuda.synchronize()
         for what, call in launches:
             with torch.cuda.stream(stream):
@@ -801,7 +805,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "k_reduce<8, true, 4, false> (write mode, P = 8): 1100 x 64 lanes",
+                     "kernel": "k_reduce<8, true, 4, true, false> (write mode, P = 8, non-temporal "
+                               "loads and stores): 1100 x 64 lanes",
                      "mean_launch_us": round(ms * 1e3, 3),
                      "per_call_event_pair_us": round(per_call["mean_us"], 3),
                      "regime": "HBM-resident: each call's inputs and outputs were last touched "

@@ -300,10 +300,13 @@ int ar_noop(void *stream);
  * 16-byte stores with the same cache policy, `unroll` vectors in flight per
  * lane (1 or 2 for kind 0; 1, 2 or 4 otherwise), `threads` in {64, 128, 256}
  * lanes per workgroup, `blocks` workgroups at most (0: one pass, one vector
- * per lane per unroll step).  P is 4 or 8; n elements per buffer, a multiple
- * of 8, at most 2^29; every buffer 16-byte aligned and none overlapping. */
+ * per lane per unroll step), and either cache policy the reduce kernels use
+ * (`policy` 0: plain loads, device-scope write-through streaming stores;
+ * 1: non-temporal loads and stores).  P is 4 or 8; n elements per buffer, a
+ * multiple of 8, at most 2^29; every buffer 16-byte aligned and none
+ * overlapping. */
 int ar_probe_traffic(int kind, ar_ptrs in, ar_ptrs out, int P, int64_t n, int threads, int unroll,
-                     int blocks, void *stream);
+                     int blocks, int policy, void *stream);
 
 /* Benchmark-only launch-shape overrides (process-global, not thread-safe).
  * ar_set_reduce_tuning: unroll (vectors in flight per lane) in {0 = automatic,

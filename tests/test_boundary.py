@@ -374,15 +374,16 @@ def test_probe_traffic_validation():
     ins, outs = _bufs(8), _bufs(8, base=FAKE + (1 << 30))
     L = ar.lib()
     P_ = ar._ptrs
-    ok = (P_(ins), P_(outs), 8, 4096, 64, 1, 0, STREAM)
+    ok = (P_(ins), P_(outs), 8, 4096, 64, 1, 0, 0, STREAM)
     assert L.ar_probe_traffic(3, *ok) == ar.AR_EINVAL                              # kind
-    assert L.ar_probe_traffic(0, P_(ins), P_(outs), 8, 4096, 64, 4, 0, STREAM) == ar.AR_EINVAL
-    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 3, 4096, 64, 1, 0, STREAM) == ar.AR_EINVAL
-    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 8, 4095, 64, 1, 0, STREAM) == ar.AR_EINVAL
-    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 8, 4096, 96, 1, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 8, 4096, 64, 1, 0, 2, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(0, P_(ins), P_(outs), 8, 4096, 64, 4, 0, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 3, 4096, 64, 1, 0, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 8, 4095, 64, 1, 0, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(1, P_(ins), P_(outs), 8, 4096, 96, 1, 0, 0, STREAM) == ar.AR_EINVAL
     bad = list(outs)
     bad[3] = ins[5] + 64                                                          # overlap
-    assert L.ar_probe_traffic(2, P_(ins), P_(bad), 8, 4096, 64, 1, 0, STREAM) == ar.AR_EALIAS
+    assert L.ar_probe_traffic(2, P_(ins), P_(bad), 8, 4096, 64, 1, 0, 0, STREAM) == ar.AR_EALIAS
     bad = list(ins)
     bad[1] = ins[1] + 8                                                           # not 16-B
-    assert L.ar_probe_traffic(2, P_(bad), P_(outs), 8, 4096, 64, 1, 0, STREAM) == ar.AR_EINVAL
+    assert L.ar_probe_traffic(2, P_(bad), P_(outs), 8, 4096, 64, 1, 0, 0, STREAM) == ar.AR_EINVAL
