@@ -45,6 +45,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only-headline      (profiling runs: the headline only)
        python bench.py --copy-probe         (counter calibration: a plain copy)
        python bench.py --ceilings           (profiling runs: same-size ceilings, cold)
+       python bench.py --shape-sweep        (profiling runs: reduce launch shapes, cold)
 """
 from __future__ import annotations
 
@@ -502,6 +503,57 @@ def ceilings_mode(torch, ar, I, W, stream, reps=12):
             "bytes": {c[0]: 2 * P * c[1] * 2 for c in cases}}
 
 
+# (unroll, threads, max_blocks, schedule) launch shapes of the reduce kernels
+# compared by --shape-sweep; (0, 0, 0, 0) is the automatic choice
+SWEEP_SHAPES = [(0, 0, 0, 0), (1, 64, 0, 1), (2, 64, 0, 1), (4, 64, 0, 1), (1, 128, 0, 1),
+                (2, 128, 0, 1), (1, 256, 0, 1), (2, 256, 0, 1), (2, 256, 512, 1), (1, 64, 512, 1),
+                (1, 64, 256, 1), (1, 64, 0, 2), (1, 128, 0, 2), (1, 64, 0, 4), (2, 64, 0, 2)]
+
+
+def shape_sweep_mode(torch, ar, I, W, stream, reps=12):
+    """--shape-sweep: the reduce kernels' launch shapes (ar_set_reduce_tuning)
+    on the write-mode headline and on the two-shot share of rank 3 of
+    680x5120 x 8, each launch right after a 512 MiB read-only scrub (run under
+    rocprofv3 --kernel-trace for each launch's cold duration; `order` lists
+    the timed launches in dispatch order, after one check call per shape),
+    plus the headline over 8 rotating buffer sets, back to back, per shape."""
+    P_, s = ar._ptrs, int(stream.cuda_stream)
+    scrub = torch.ones(512 << 20, dtype=torch.uint8, device="cuda:0")
+    hl, r3 = W.WRITE_BCAST_440x5120, W.TWOSHOT_680x5120_R3
+    x_hl = [torch.from_numpy(x.view("int16")).to("cuda:0") for x in I.make_inputs(hl.dist, hl.P, hl.n)]
+    o_hl = [torch.empty(hl.n, dtype=torch.int16, device="cuda:0") for _ in range(hl.P)]
+    x_r3 = [torch.from_numpy(x.view("int16")).to("cuda:0") for x in I.make_inputs(r3.dist, r3.P, r3.n)]
+    o_r3 = [torch.empty(r3.n, dtype=torch.int16, device="cuda:0") for _ in range(r3.P)]
+    order, rotating = [], {}
+    try:
+        for label, mk in (("write_bcast_440x5120_p8",
+                           lambda: _raw(ar, "ar_oneshot_write_bcast", P_(x_hl), P_(o_hl), hl.P, hl.n, s)),
+                          ("twoshot_680x5120_p8_rank3",
+                           lambda: _raw(ar, "ar_twoshot_share", P_(x_r3), P_(o_r3), r3.P, 3, r3.n, s))):
+            for shape in SWEEP_SHAPES:
+                ar.ar_set_reduce_tuning(*shape)
+                call = mk()                      # one check call, not timed
+                torch.cuda.synchronize()
+                with torch.cuda.stream(stream):
+                    for _ in range(reps):
+                        scrub.view(torch.int32).amax()
+                        call()
+                        order.append([label, list(shape)])
+                torch.cuda.synchronize()
+        rot = RotatingSets(torch, ar, stream, hl, x_hl)
+        for shape in SWEEP_SHAPES:
+            ar.ar_set_reduce_tuning(*shape)
+            calls = [_raw(ar, "ar_oneshot_write_bcast", P_(i), P_(o), hl.P, hl.n, s)
+                     for i, o in zip(rot.ins, rot.outs)]
+            ms, _ = time_streamed(torch, stream, lambda i: calls[i % rot.sets](), 300, 16)
+            rotating[str(shape)] = round(ms * 1e3, 3)
+    finally:
+        ar.ar_set_reduce_tuning(0, 0, 0, 0)
+    return {"order": order, "rotating_us_440x5120_p8": rotating,
+            "bytes": {"write_bcast_440x5120_p8": 2 * hl.P * hl.n * 2,
+                      "twoshot_680x5120_p8_rank3": 2 * r3.P * 435200 * 2}}
+
+
 def time_copy_reference(torch, stream, nbytes, steps, sets=8):
     """A plain device copy (torch's copy_, i.e. the runtime's own copy kernel)
     of `nbytes`, which moves the same bytes as the headline when nbytes is its
@@ -721,6 +773,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true")
     ap.add_argument("--rows", default="", help="comma-separated workload names (default: all)")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--shape-sweep", action="store_true",
+                    help="profiling: the reduce kernels' launch shapes, cold (after a 512 MiB "
+                         "scrub) and over rotating sets")
     ap.add_argument("--ceilings", action="store_true",
                     help="profiling: probe kernels and the library's call, each right after a "
                          "512 MiB scrub (cold), plus the rotating-set ceilings")
@@ -757,6 +812,9 @@ def main():
 
     if args.ceilings:
         print(json.dumps(ceilings_mode(torch, ar, I, W, stream)), flush=True)
+        return
+    if args.shape_sweep:
+        print(json.dumps(shape_sweep_mode(torch, ar, I, W, stream)), flush=True)
         return
 
     headline = W.WRITE_BCAST_440x5120
