@@ -154,6 +154,30 @@ int main(int argc, char **argv)
         HIP_OK(hipMemcpy(chk, out2.p[p], bytes, hipMemcpyDeviceToHost));
         if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "epoch output %d differs\n", p); return 5; }
     }
+    /* no-alloc packet share: the library's own scratch; beyond its size the
+     * call must refuse with AR_ENOSPACE before touching the GPU */
+    int32_t *st = NULL;
+    HIP_OK(hipMalloc((void **)&st, sizeof *st));
+    HIP_OK(hipMemset(st, 0x5A, sizeof *st));
+    for (int p = 0; p < P; ++p) HIP_OK(hipMemset(out2.p[p], 0, bytes));
+    const int64_t per_rank = (ar_packet_scratch_bytes(P, n) + 255) / 256 * 256;
+    const int fits = 256 + (int64_t)P * per_rank <= (int64_t)AR_NOALLOC_SCRATCH_BYTES;
+    const int nrc = ar_packet_fused_noalloc(in, out2, P, n, st, 0, s);
+    if (!fits) {
+        if (nrc != AR_ENOSPACE) { fprintf(stderr, "no-alloc: expected AR_ENOSPACE, got %d\n", nrc); return 6; }
+    } else {
+        AR_OK_(nrc);
+        HIP_OK(hipStreamSynchronize(s));
+        int32_t hs = -1;
+        HIP_OK(hipMemcpy(&hs, st, sizeof hs, hipMemcpyDeviceToHost));
+        if (hs != AR_OK) { fprintf(stderr, "no-alloc status %s\n", ar_strerror(hs)); return 4; }
+        for (int p = 0; p < P; ++p) {
+            HIP_OK(hipMemcpy(chk, out2.p[p], bytes, hipMemcpyDeviceToHost));
+            if (memcmp(chk, res, bytes) != 0) { fprintf(stderr, "no-alloc output %d differs\n", p); return 5; }
+        }
+    }
+    HIP_OK(hipFree(st));
+
     f = fopen(argv[4], "wb");
     if (!f || fwrite(res, 2, (size_t)n, f) != (size_t)n) return 1;
     fclose(f);

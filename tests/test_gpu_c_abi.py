@@ -1,7 +1,8 @@
 """The C ABI driven from plain C (tests/c_abi_check.c): raw hipMalloc'd
 device pointers, one stream, no PyTorch in the call path.  The program checks
-that every entry point agrees with write mode; this test checks
-its result against the CPU oracle."""
+that every entry point agrees with write mode (the no-alloc packet share
+where it fits the library's static scratch, AR_ENOSPACE where it does not);
+this test checks its result against the CPU oracle."""
 from __future__ import annotations
 
 import pathlib
