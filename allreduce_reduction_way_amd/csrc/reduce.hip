@@ -88,15 +88,15 @@ __device__ __forceinline__ void scalar_part(const ReduceArgs &a, int64_t tid, in
 // vector-memory counter retires loads and stores in issue order, so waiting
 // for those loads also waits for the stores to be acknowledged.
 //
-// U = 4 is the one-pass shape for data coming from HBM: all 4P loads of a
-// lane are issued before any store.  It takes non-temporal loads and
-// non-temporal stores without the device-scope write-through at every size
-// (NTL and WT are fixed by pick_unroll): measured on MI355X in one process,
-// interleaved, the write-mode share of 440x5120 x 8 ran 13.86 us per call
-// from HBM against 14.33 us with plain loads and write-through stores
-// (14.22 with NT loads alone, 14.24 with NT stores alone), and 10.79 against
-// 10.96 us back to back on one buffer set; on a second box 14.18 against
-// 14.55 us from HBM and 13.92 against 14.56 us cold (after a 512 MiB scrub).
+// U = 4 takes non-temporal loads and non-temporal stores without the
+// device-scope write-through at every size (NTL and WT are fixed by
+// pick_unroll), as does k_reduce_phased below, which replaced it as the
+// automatic one-pass shape: measured on MI355X in one process, interleaved,
+// the write-mode share of 440x5120 x 8 ran 13.86 us per call from HBM against
+// 14.33 us with plain loads and write-through stores (14.22 with NT loads
+// alone, 14.24 with NT stores alone), and 10.79 against 10.96 us back to back
+// on one buffer set; on a second box 14.18 against 14.55 us from HBM and
+// 13.92 against 14.56 us cold (after a 512 MiB scrub).
 template <int P, bool BCAST, int U, bool NTL, bool WT>
 __global__ __launch_bounds__(kThreads) void k_reduce(ReduceArgs a) {
     const int64_t nth = (int64_t)gridDim.x * blockDim.x;
@@ -161,12 +161,61 @@ __global__ __launch_bounds__(kThreads) void k_reduce_pipe(ReduceArgs a) {
     scalar_part<P, BCAST>(a, tid, (int64_t)gridDim.x * blockDim.x);
 }
 
+// One pass in three phases: global wave g (64 lanes) owns the U x 64
+// consecutive vectors from g x U x 64 of every buffer -- at U = 4 that is
+// 4 KiB of each input and each output -- and issues all U x P loads, then all
+// U reductions, then all U x NOUT stores.  The scheduling barriers keep the
+// compiler from starting a vector's stores while the wave still has loads to
+// wait for.  Every wave therefore reads before it writes, and with every wave
+// of the grid resident at once the device sees mostly reads first and
+// mostly writes last, instead of the two mixed.  Measured on MI355X, write
+// mode 440x5120 x 8 from HBM (buffer sets rotated through 576 MB), in one
+// process, interleaved:
+//  - 13.34 us per call against 13.64 us for the same loads and stores with a
+//    stride of one grid between a lane's vectors;
+//  - against 15.79 us when each vector's stores follow its own loads as soon
+//    as they arrive (exact waits, so reads and writes overlap);
+//  - 64-lane workgroups: the same layout in 256-lane workgroups ran 16.4 us.
+// As in k_reduce_pipe, no memory instruction sits behind a branch: lanes past
+// the bulk load the last vector again (in bounds) and store at an offset past
+// the buffer resource's range, which the hardware drops.
+template <int P, bool BCAST, int U>
+__global__ __launch_bounds__(kThreads) void k_reduce_phased(ReduceArgs a) {
+    constexpr int NOUT = BCAST ? P : 1;
+    const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a.nvec > 0) {
+        const int64_t base = (gtid >> 6) * (64 * U) + (gtid & 63);
+        u32x4 x[U][P];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t w = base + 64 * u;
+            w = w < a.nvec ? w : a.nvec - 1;
+#pragma unroll
+            for (int p = 0; p < P; ++p) x[u][p] = load_vec<true>(a.in.p[p], a.head + 8 * w);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        u32x4 r[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) r[u] = reduce_vec<P>(x[u]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t w = base + 64 * u;
+            const uint32_t off = w < a.nvec ? (uint32_t)(2 * (a.head + 8 * w)) : kDroppedStoreOffset;
+#pragma unroll
+            for (int o = 0; o < NOUT; ++o) store_vec<false>(a.out.p[o], off, r[u]);
+        }
+    }
+    scalar_part<P, BCAST>(a, gtid, (int64_t)gridDim.x * blockDim.x);
+}
+
 // ---- kernel table ------------------------------------------------------------
 
 typedef void (*ReduceKernel)(ReduceArgs);
 
-// Schedules: kBatch grid-stride batches; kPipe2/4/8 pipelined, that many stages.
-enum Schedule { kBatch = 1, kPipe2 = 2, kPipe4 = 4, kPipe8 = 8 };
+// Schedules: kBatch grid-stride batches; kPipe2/4/8 pipelined, that many
+// stages; kPhased one pass, loads then reductions then stores.
+enum Schedule { kBatch = 1, kPipe2 = 2, kPipe4 = 4, kPipe8 = 8, kPhased = 16 };
 
 inline bool is_pipe(int sched) { return sched == kPipe2 || sched == kPipe4 || sched == kPipe8; }
 
@@ -177,6 +226,9 @@ ReduceKernel pick_pipe_unroll(int U) {
 
 template <int P, bool BCAST, bool NTL>
 ReduceKernel pick_unroll(int U, int sched) {
+    if (sched == kPhased)
+        return U == 1 ? k_reduce_phased<P, BCAST, 1>
+                      : (U == 2 ? k_reduce_phased<P, BCAST, 2> : k_reduce_phased<P, BCAST, 4>);
     switch (sched) {
         case kPipe2: return pick_pipe_unroll<P, BCAST, NTL, 2>(U);
         case kPipe4: return pick_pipe_unroll<P, BCAST, NTL, 4>(U);
@@ -259,42 +311,36 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
     split_range(in_at, out_at, P, bcast ? P : 1, len, &a);
 
     // Launch shape, chosen from sweeps on MI355X with the data coming from HBM
-    // (buffer sets rotated through 576 MB or more, and single calls after a
-    // 512 MiB scrub), by the bulk's 16-byte vectors per input:
+    // (buffer sets rotated through 576 MB or more, interleaved in one process),
+    // by the bulk's 16-byte vectors per input (per CU: 256 CUs):
     //  - up to 256 per CU: latency-bound; one vector per lane in 64-lane
     //    workgroups, so the work spreads over every CU;
     //  - up to 768 per CU, P >= 4: the pipelined kernel in two stages, 64-lane
     //    workgroups (1M elements x 8 / x 4: 6.2 / 3.9 us instead of 6.7 / 4.1);
-    //  - up to 2560 per CU, P = 8: one pass, four vectors per lane per input
-    //    (32 loads in flight per lane) in 64-lane workgroups, about one wave per
-    //    SIMD: the write-mode share of 440x5120 x 8 runs 14.0-14.4 us from HBM
-    //    instead of 15.1-15.9 us (13.4 instead of 15.9 us cold);
-    //  - beyond: 256-lane workgroups, two vectors in flight per lane, exactly
-    //    two workgroups per CU, grid stride (a grid that is a multiple of the
-    //    CU count keeps the CUs evenly loaded).
+    //  - up to 2560 per CU: one pass, four vectors per lane per input (4P loads
+    //    in flight per lane) in 64-lane workgroups, every load before any store
+    //    (k_reduce_phased).  The write-mode share of 440x5120 x 8 runs 13.3 us,
+    //    against 14.1-14.3 us for the same loads in grid-stride batches and
+    //    16.4-16.9 us for 256-lane workgroups with two vectors per lane; at
+    //    x 4, 7.0 against 8.2-8.5 us; 3M elements x 4 8.8 against 10.2 us;
+    //  - beyond: the two-stage pipelined kernel in 64-lane workgroups, one
+    //    vector per lane per stage, a grid that covers the bulk: 16M elements
+    //    x 4 (one owner of the 64 Mi two-shot) 47.9 against 51.0 us for 256-lane
+    //    grid-stride batches, x 8 103.4 against 110.2 us, x 6 72.1 against 78.2.
     // With the data in the MALL instead (back-to-back calls on one buffer set
-    // of up to 256 MB) the last shape is faster (9.4 against 11.2 us for the
-    // 440x5120 x 8 share); the automatic choice is made for data from HBM.
-    int threads, U, sched = kBatch;
-    int64_t blocks;
+    // of up to 256 MB) grid-stride batches are faster (9.4 against 11.2 us for
+    // the 440x5120 x 8 share); the automatic choice is made for data from HBM.
+    int threads = 64, U = 1, sched = kBatch;
+    int64_t blocks = 0;  // 0: the grid covers the bulk (set below)
     if (a.nvec <= (int64_t)dev.cus * 256) {
-        threads = 64;
-        U = 1;
         blocks = (a.nvec + threads - 1) / threads;
     } else if (P >= 4 && a.nvec <= (int64_t)dev.cus * 768) {
-        threads = 64;
-        U = 1;
         sched = kPipe2;
-        blocks = 0;  // set below: the pipelined grid covers the bulk
-    } else if (P == 8 && a.nvec <= (int64_t)dev.cus * 2560) {
-        threads = 64;
+    } else if (a.nvec <= (int64_t)dev.cus * 2560) {
         U = 4;
-        blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
+        sched = kPhased;
     } else {
-        threads = kThreads;
-        U = 2;
-        blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
-        if (blocks > 2 * (int64_t)dev.cus) blocks = 2 * (int64_t)dev.cus;
+        sched = kPipe2;
     }
     if (g_unroll_override == 1 || g_unroll_override == 2 || g_unroll_override == 4) {
         U = g_unroll_override;
@@ -309,6 +355,10 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
         // no grid stride: the grid covers the bulk, sched stages of U vectors per lane
         if (U > 2) U = 2;
         const int64_t per_block = (int64_t)threads * U * sched;
+        blocks = (a.nvec + per_block - 1) / per_block;
+    } else if (sched == kPhased) {
+        // no grid stride: the grid covers the bulk, U vectors per lane
+        const int64_t per_block = (int64_t)threads * U;
         blocks = (a.nvec + per_block - 1) / per_block;
     } else {
         if (blocks == 0) blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
@@ -427,7 +477,7 @@ int ar_reduce_scatter_share(ar_ptrs in, void *out, int P, int rank, int64_t recv
 int ar_set_reduce_tuning(int unroll, int threads, int max_blocks, int schedule) {
     if (!(unroll == 0 || unroll == 1 || unroll == 2 || unroll == 4) || max_blocks < 0 ||
         !(threads == 0 || threads == 64 || threads == 128 || threads == 256) ||
-        !(schedule == 0 || schedule == kBatch || is_pipe(schedule)) ||
+        !(schedule == 0 || schedule == kBatch || is_pipe(schedule) || schedule == kPhased) ||
         (is_pipe(schedule) && unroll == 4))
         return AR_EINVAL;
     g_unroll_override = unroll;

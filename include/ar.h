@@ -314,9 +314,12 @@ int ar_probe_traffic(int kind, ar_ptrs in, ar_ptrs out, int P, int64_t n, int th
  * workgroups (0 = automatic; batches only) and the schedule (0 = automatic,
  * 1 = grid-stride batches: load U vectors, then store them; 2, 4 or 8 =
  * pipelined in that many stages of U vectors per lane, the next stage's loads
- * issued before the current stores, unroll 1 or 2) for ar_oneshot_sum,
- * ar_oneshot_write_bcast, ar_twoshot_share and ar_reduce_scatter_share.  ar_set_packet_tuning: workgroups per emulated rank of
- * ar_packet_fused (0 = automatic; never more than fit on the device at once)
+ * issued before the current stores, unroll 1 or 2; 16 = one pass in which
+ * global wave g takes the U x 64 consecutive vectors from g x U x 64, all its
+ * loads issued before any reduction and every reduction before any store) for
+ * ar_oneshot_sum, ar_oneshot_write_bcast, ar_twoshot_share and
+ * ar_reduce_scatter_share.  ar_set_packet_tuning: workgroups per emulated rank
+ * of ar_packet_fused (0 = automatic; never more than fit on the device at once)
  * words per lane per chunk in {0 = automatic, 1, 2}, and the schedule of
  * ar_packet_fused: 0 = every workgroup runs all phases of its chunks as a
  * pipeline, 1 = separate scatter, reduce-broadcast and receive workgroups in

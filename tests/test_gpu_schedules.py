@@ -1,6 +1,7 @@
 """GPU parity of the reduce entry points under every launch schedule the
-library can take (grid-stride batches, and the pipelined kernel with 2, 4 or 8
-stages of 1 or 2 vectors per lane, for 64/128/256-lane workgroups), forced
+library can take (grid-stride batches, the pipelined kernel with 2, 4 or 8
+stages of 1 or 2 vectors per lane, and the phased one-pass kernel with 1, 2 or
+4 vectors per lane, for 64/128/256-lane workgroups), forced
 through the benchmark tuning hook.  Results must not depend on the schedule:
 bit-exact against the oracle, guard bands intact, in place included.  Sizes
 leave ragged last workgroups, partial stages and scalar heads and tails."""
@@ -20,7 +21,8 @@ pytestmark = pytest.mark.gpu
 SHAPES = [(1, 64, 0, 1), (2, 256, 7, 1), (4, 128, 0, 1),
           (1, 64, 0, 2), (2, 64, 0, 2), (1, 256, 0, 2), (2, 128, 0, 2),
           (1, 64, 0, 4), (2, 64, 0, 4), (1, 128, 0, 4), (2, 256, 0, 4),
-          (1, 64, 0, 8), (2, 64, 0, 8), (1, 256, 0, 8)]
+          (1, 64, 0, 8), (2, 64, 0, 8), (1, 256, 0, 8),
+          (1, 64, 0, 16), (2, 64, 0, 16), (4, 64, 0, 16), (2, 128, 0, 16), (4, 256, 0, 16)]
 # vectors per workgroup-stage for 64 lanes = 64; 2 x 64 x 8 x 5 + 3 leaves a ragged stage
 SIZES = [1, 9, 8 * 64 * 3 + 5, 8 * 2 * 64 * 8 * 5 + 3 * 8 + 5, 100_003]
 
@@ -96,8 +98,9 @@ def test_twoshot_and_reduce_scatter_every_schedule(tuning, shape):
 # (256 CUs: 524,288, 1,572,864 and 5,242,880 elements); sizes on both sides.
 @pytest.mark.parametrize("P,n", [(8, 524_288 - 8), (8, 524_288 + 9), (4, 524_288 + 9),
                                  (8, 1_572_864 - 3), (5, 1_572_864 - 3), (3, 1_000_003),
-                                 (8, 1_572_864 + 11), (8, 5_242_880 - 7), (8, 5_242_880 + 5),
-                                 (7, 2_252_800 + 1)])
+                                 (8, 1_572_864 + 11), (2, 1_572_864 + 11),
+                                 (8, 5_242_880 - 7), (8, 5_242_880 + 5), (3, 5_242_880 + 5),
+                                 (6, 5_242_880 - 7), (7, 2_252_800 + 1)])
 def test_automatic_shape_classes(P, n):
     ar.ar_set_reduce_tuning(0, 0, 0, 0)
     for shift in (0, 5):
