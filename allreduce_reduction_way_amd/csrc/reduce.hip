@@ -144,46 +144,52 @@ __device__ __forceinline__ void store_stage_masked(const ReduceArgs &a, int64_t 
     }
 }
 
+//
+// The bulk is never empty here (launch_piece takes the batch kernel for a call
+// with no 16-byte vectors), so the kernel needs no guard around it: a guard
+// made the compiler wait for the vector count before it fetched the pointer
+// table, two dependent rounds of kernel-argument loads before the first
+// global load of every wave, where one is enough.
 template <int P, bool BCAST, int U, int S, bool NTL>
 __global__ __launch_bounds__(kThreads) void k_reduce_pipe(ReduceArgs a) {
     const int64_t bd = blockDim.x;
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (a.nvec > 0) {
-        const int64_t v0 = (int64_t)blockIdx.x * S * U * bd + threadIdx.x;
-        u32x4 x[2][U][P];
-        load_stage_clamped<P, U, NTL>(a, v0, bd, x[0]);
+    const int64_t v0 = (int64_t)blockIdx.x * S * U * bd + threadIdx.x;
+    u32x4 x[2][U][P];
+    load_stage_clamped<P, U, NTL>(a, v0, bd, x[0]);
 #pragma unroll
-        for (int k = 0; k < S; ++k) {
-            if (k + 1 < S) load_stage_clamped<P, U, NTL>(a, v0 + (k + 1) * U * bd, bd, x[(k + 1) & 1]);
-            store_stage_masked<P, BCAST, U>(a, v0 + k * U * bd, bd, x[k & 1]);
-        }
+    for (int k = 0; k < S; ++k) {
+        if (k + 1 < S) load_stage_clamped<P, U, NTL>(a, v0 + (k + 1) * U * bd, bd, x[(k + 1) & 1]);
+        store_stage_masked<P, BCAST, U>(a, v0 + k * U * bd, bd, x[k & 1]);
     }
     scalar_part<P, BCAST>(a, tid, (int64_t)gridDim.x * blockDim.x);
 }
 
 // One pass in three phases: global wave g (64 lanes) owns the U x 64
-// consecutive vectors from g x U x 64 of every buffer -- at U = 4 that is
-// 4 KiB of each input and each output -- and issues all U x P loads, then all
+// consecutive vectors from g x U x 64 of every buffer -- at U = 5 that is
+// 5 KiB of each input and each output -- and issues all U x P loads, then all
 // U reductions, then all U x NOUT stores.  The scheduling barriers keep the
 // compiler from starting a vector's stores while the wave still has loads to
 // wait for.  Every wave therefore reads before it writes, and with every wave
 // of the grid resident at once the device sees mostly reads first and
 // mostly writes last, instead of the two mixed.  Measured on MI355X, write
 // mode 440x5120 x 8 from HBM (buffer sets rotated through 576 MB), in one
-// process, interleaved:
+// process, interleaved, at U = 4:
 //  - 13.34 us per call against 13.64 us for the same loads and stores with a
 //    stride of one grid between a lane's vectors;
 //  - against 15.79 us when each vector's stores follow its own loads as soon
 //    as they arrive (exact waits, so reads and writes overlap);
 //  - 64-lane workgroups: the same layout in 256-lane workgroups ran 16.4 us.
+// launch_piece picks U (see there); at U = 5 the same share runs 12.0 us.
 // As in k_reduce_pipe, no memory instruction sits behind a branch: lanes past
 // the bulk load the last vector again (in bounds) and store at an offset past
-// the buffer resource's range, which the hardware drops.
+// the buffer resource's range, which the hardware drops; and the bulk is
+// never empty.
 template <int P, bool BCAST, int U>
 __global__ __launch_bounds__(kThreads) void k_reduce_phased(ReduceArgs a) {
     constexpr int NOUT = BCAST ? P : 1;
     const int64_t gtid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (a.nvec > 0) {
+    {
         const int64_t base = (gtid >> 6) * (64 * U) + (gtid & 63);
         u32x4 x[U][P];
 #pragma unroll
@@ -224,11 +230,29 @@ ReduceKernel pick_pipe_unroll(int U) {
     return U == 1 ? k_reduce_pipe<P, BCAST, 1, S, NTL> : k_reduce_pipe<P, BCAST, 2, S, NTL>;
 }
 
+// Most vectors per lane k_reduce_phased takes for P inputs: a lane holds
+// U x P loaded vectors (4 VGPRs each), and past 48 of them a wave outgrows
+// 256 VGPRs.
+constexpr int phased_max_unroll(int P) { return P >= 7 ? 6 : 8; }
+
+template <int P, bool BCAST>
+ReduceKernel pick_phased(int U) {
+    constexpr int M = phased_max_unroll(P);
+    switch (U < M ? U : M) {
+        case 1: return k_reduce_phased<P, BCAST, 1>;
+        case 2: return k_reduce_phased<P, BCAST, 2>;
+        case 3: return k_reduce_phased<P, BCAST, 3>;
+        case 4: return k_reduce_phased<P, BCAST, 4>;
+        case 5: return k_reduce_phased<P, BCAST, 5>;
+        case 6: return k_reduce_phased<P, BCAST, 6>;
+        case 7: return k_reduce_phased<P, BCAST, (M >= 7 ? 7 : M)>;
+        default: return k_reduce_phased<P, BCAST, M>;
+    }
+}
+
 template <int P, bool BCAST, bool NTL>
 ReduceKernel pick_unroll(int U, int sched) {
-    if (sched == kPhased)
-        return U == 1 ? k_reduce_phased<P, BCAST, 1>
-                      : (U == 2 ? k_reduce_phased<P, BCAST, 2> : k_reduce_phased<P, BCAST, 4>);
+    if (sched == kPhased) return pick_phased<P, BCAST>(U);
     switch (sched) {
         case kPipe2: return pick_pipe_unroll<P, BCAST, NTL, 2>(U);
         case kPipe4: return pick_pipe_unroll<P, BCAST, NTL, 4>(U);
@@ -312,17 +336,22 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
 
     // Launch shape, chosen from sweeps on MI355X with the data coming from HBM
     // (buffer sets rotated through 576 MB or more, interleaved in one process),
-    // by the bulk's 16-byte vectors per input (per CU: 256 CUs):
-    //  - up to 256 per CU: latency-bound; one vector per lane in 64-lane
-    //    workgroups, so the work spreads over every CU;
-    //  - up to 768 per CU, P >= 4: the pipelined kernel in two stages, 64-lane
+    // by the bulk's 16-byte vectors per input per CU (vpc; 256 CUs, 1024 SIMDs):
+    //  - vpc <= 256: latency-bound; one vector per lane in 64-lane workgroups,
+    //    so the work spreads over every CU;
+    //  - vpc <= 768, P >= 4: the pipelined kernel in two stages, 64-lane
     //    workgroups (1M elements x 8 / x 4: 6.2 / 3.9 us instead of 6.7 / 4.1);
-    //  - up to 2560 per CU: one pass, four vectors per lane per input (4P loads
-    //    in flight per lane) in 64-lane workgroups, every load before any store
-    //    (k_reduce_phased).  The write-mode share of 440x5120 x 8 runs 13.3 us,
-    //    against 14.1-14.3 us for the same loads in grid-stride batches and
-    //    16.4-16.9 us for 256-lane workgroups with two vectors per lane; at
-    //    x 4, 7.0 against 8.2-8.5 us; 3M elements x 4 8.8 against 10.2 us;
+    //  - vpc <= 2560: one pass, every load before any store (k_reduce_phased),
+    //    64-lane workgroups.  U, the vectors per lane per input, is the
+    //    smallest that leaves at most one wave per SIMD (U = ceil(vpc / 256)),
+    //    as far as the registers allow: the write-mode share of 440x5120 x 8
+    //    (vpc 1100) runs 12.0-12.1 us with U = 5 (880 waves) against
+    //    13.4-14.0 us with U = 4 (1100 waves, so 76 SIMDs run two) and 12.7
+    //    with U = 6 (733 waves).  Past the register limit P = 8 takes U = 5
+    //    (2048 vpc: 25.3 us against 28.0 with U = 6), P = 7 U = 6.  P <= 4
+    //    keeps U = 4 up to vpc 1536 (x 4 at 1536: 8.7 us against 9.3 with
+    //    U = 6), then one wave per SIMD up to U = 8 (x 4 at 2560: 14.1 us
+    //    against 16.0 with U = 4);
     //  - beyond: the two-stage pipelined kernel in 64-lane workgroups, one
     //    vector per lane per stage, a grid that covers the bulk: 16M elements
     //    x 4 (one owner of the 64 Mi two-shot) 47.9 against 51.0 us for 256-lane
@@ -332,17 +361,23 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
     // the 440x5120 x 8 share); the automatic choice is made for data from HBM.
     int threads = 64, U = 1, sched = kBatch;
     int64_t blocks = 0;  // 0: the grid covers the bulk (set below)
-    if (a.nvec <= (int64_t)dev.cus * 256) {
+    const int64_t vpc = (a.nvec + dev.cus - 1) / dev.cus;
+    if (vpc <= 256) {
         blocks = (a.nvec + threads - 1) / threads;
-    } else if (P >= 4 && a.nvec <= (int64_t)dev.cus * 768) {
+    } else if (P >= 4 && vpc <= 768) {
         sched = kPipe2;
-    } else if (a.nvec <= (int64_t)dev.cus * 2560) {
-        U = 4;
+    } else if (vpc <= 2560) {
         sched = kPhased;
+        const int one_wave_per_simd = (int)((vpc + 255) / 256);
+        if (P >= 5)
+            U = one_wave_per_simd <= phased_max_unroll(P) ? one_wave_per_simd
+                                                          : (P == 8 ? 5 : phased_max_unroll(P));
+        else
+            U = vpc <= 1536 ? 4 : (one_wave_per_simd < 8 ? one_wave_per_simd : 8);
     } else {
         sched = kPipe2;
     }
-    if (g_unroll_override == 1 || g_unroll_override == 2 || g_unroll_override == 4) {
+    if (g_unroll_override > 0) {
         U = g_unroll_override;
         blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
     }
@@ -351,6 +386,12 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
         blocks = (a.nvec + (int64_t)threads * U - 1) / ((int64_t)threads * U);
     }
     if (g_schedule_override != 0) sched = g_schedule_override;
+    // the pipelined and phased kernels assume a non-empty bulk
+    if (a.nvec == 0 && sched != kBatch) {
+        sched = kBatch;
+        U = 1;
+        blocks = 0;
+    }
     if (is_pipe(sched)) {
         // no grid stride: the grid covers the bulk, sched stages of U vectors per lane
         if (U > 2) U = 2;
@@ -358,6 +399,7 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
         blocks = (a.nvec + per_block - 1) / per_block;
     } else if (sched == kPhased) {
         // no grid stride: the grid covers the bulk, U vectors per lane
+        if (U > phased_max_unroll(P)) U = phased_max_unroll(P);
         const int64_t per_block = (int64_t)threads * U;
         blocks = (a.nvec + per_block - 1) / per_block;
     } else {
@@ -475,10 +517,11 @@ int ar_reduce_scatter_share(ar_ptrs in, void *out, int P, int rank, int64_t recv
 
 // Benchmark-only launch-shape override for the reduce entry points above.
 int ar_set_reduce_tuning(int unroll, int threads, int max_blocks, int schedule) {
-    if (!(unroll == 0 || unroll == 1 || unroll == 2 || unroll == 4) || max_blocks < 0 ||
+    const bool batch_unroll = unroll == 0 || unroll == 1 || unroll == 2 || unroll == 4;
+    if (unroll < 0 || unroll > 8 || max_blocks < 0 ||
         !(threads == 0 || threads == 64 || threads == 128 || threads == 256) ||
         !(schedule == 0 || schedule == kBatch || is_pipe(schedule) || schedule == kPhased) ||
-        (is_pipe(schedule) && unroll == 4))
+        (schedule != kPhased && !batch_unroll) || (is_pipe(schedule) && unroll == 4))
         return AR_EINVAL;
     g_unroll_override = unroll;
     g_threads_override = threads;

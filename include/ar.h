@@ -310,7 +310,8 @@ int ar_probe_traffic(int kind, ar_ptrs in, ar_ptrs out, int P, int64_t n, int th
 
 /* Benchmark-only launch-shape overrides (process-global, not thread-safe).
  * ar_set_reduce_tuning: unroll (vectors in flight per lane) in {0 = automatic,
- * 1, 2, 4}, workgroup size in {0 = automatic, 64, 128, 256}, a cap on
+ * 1, 2, 4} (1 to 8 with schedule 16; above 6 taken as 6 for P >= 7), workgroup
+ * size in {0 = automatic, 64, 128, 256}, a cap on
  * workgroups (0 = automatic; batches only) and the schedule (0 = automatic,
  * 1 = grid-stride batches: load U vectors, then store them; 2, 4 or 8 =
  * pipelined in that many stages of U vectors per lane, the next stage's loads

@@ -187,8 +187,11 @@ def test_tuning_validation():
     assert _err(ar.ar_set_reduce_tuning, 1, 64, 0, 3) == ar.AR_EINVAL
     assert _err(ar.ar_set_reduce_tuning, 4, 64, 0, 2) == ar.AR_EINVAL   # pipelined: unroll <= 2
     assert _err(ar.ar_set_reduce_tuning, 1, 64, 0, 32) == ar.AR_EINVAL
-    for u in (1, 2, 4):                                                  # phased: any unroll
+    for u in range(1, 9):                                                # phased: 1 to 8
         assert ar.lib().ar_set_reduce_tuning(u, 64, 0, 16) == ar.AR_OK
+    assert _err(ar.ar_set_reduce_tuning, 9, 64, 0, 16) == ar.AR_EINVAL
+    assert _err(ar.ar_set_reduce_tuning, 5, 64, 0, 1) == ar.AR_EINVAL    # batches: 1, 2 or 4
+    assert _err(ar.ar_set_reduce_tuning, 3, 64, 0, 0) == ar.AR_EINVAL
     assert _err(ar.ar_set_packet_tuning, -1, 0, 0) == ar.AR_EINVAL
     assert _err(ar.ar_set_packet_tuning, 0, 3, 0) == ar.AR_EINVAL
     assert _err(ar.ar_set_packet_tuning, 0, 0, 2) == ar.AR_EINVAL

@@ -1,7 +1,8 @@
 """GPU parity of the reduce entry points under every launch schedule the
 library can take (grid-stride batches, the pipelined kernel with 2, 4 or 8
-stages of 1 or 2 vectors per lane, and the phased one-pass kernel with 1, 2 or
-4 vectors per lane, for 64/128/256-lane workgroups), forced
+stages of 1 or 2 vectors per lane, and the phased one-pass kernel with 1 to 8
+vectors per lane, 7 and 8 taken as 6 at P >= 7, for 64/128/256-lane
+workgroups), forced
 through the benchmark tuning hook.  Results must not depend on the schedule:
 bit-exact against the oracle, guard bands intact, in place included.  Sizes
 leave ragged last workgroups, partial stages and scalar heads and tails."""
@@ -22,7 +23,9 @@ SHAPES = [(1, 64, 0, 1), (2, 256, 7, 1), (4, 128, 0, 1),
           (1, 64, 0, 2), (2, 64, 0, 2), (1, 256, 0, 2), (2, 128, 0, 2),
           (1, 64, 0, 4), (2, 64, 0, 4), (1, 128, 0, 4), (2, 256, 0, 4),
           (1, 64, 0, 8), (2, 64, 0, 8), (1, 256, 0, 8),
-          (1, 64, 0, 16), (2, 64, 0, 16), (4, 64, 0, 16), (2, 128, 0, 16), (4, 256, 0, 16)]
+          (1, 64, 0, 16), (2, 64, 0, 16), (3, 64, 0, 16), (4, 64, 0, 16), (5, 64, 0, 16),
+          (6, 64, 0, 16), (7, 64, 0, 16), (8, 64, 0, 16), (2, 128, 0, 16), (4, 256, 0, 16),
+          (5, 256, 0, 16)]
 # vectors per workgroup-stage for 64 lanes = 64; 2 x 64 x 8 x 5 + 3 leaves a ragged stage
 SIZES = [1, 9, 8 * 64 * 3 + 5, 8 * 2 * 64 * 8 * 5 + 3 * 8 + 5, 100_003]
 
