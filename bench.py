@@ -508,7 +508,8 @@ def ceilings_mode(torch, ar, I, W, stream, reps=12):
 SWEEP_SHAPES = [(0, 0, 0, 0), (1, 64, 0, 1), (2, 64, 0, 1), (4, 64, 0, 1), (1, 128, 0, 1),
                 (2, 128, 0, 1), (1, 256, 0, 1), (2, 256, 0, 1), (2, 256, 512, 1), (1, 64, 512, 1),
                 (1, 64, 256, 1), (1, 64, 0, 2), (1, 128, 0, 2), (1, 64, 0, 4), (2, 64, 0, 2),
-                (1, 64, 0, 16), (2, 64, 0, 16), (4, 64, 0, 16), (4, 128, 0, 16), (4, 256, 0, 16)]
+                (1, 64, 0, 16), (2, 64, 0, 16), (3, 64, 0, 16), (4, 64, 0, 16), (5, 64, 0, 16),
+                (6, 64, 0, 16), (4, 128, 0, 16), (4, 256, 0, 16)]
 
 
 def shape_sweep_mode(torch, ar, I, W, stream, reps=12):
