@@ -74,10 +74,14 @@ __device__ __forceinline__ uint16_t reduce_elem(const uint16_t (&e)[P]) {
 
 // ---- plain 16-byte vector I/O ---------------------------------------------
 
-// NT: non-temporal (streaming) load.  Worth it only when the data cannot stay
-// in the 256 MB MALL anyway: measured on MI355X, the 4 x 64 Mi-element
-// two-shot (268 MB per launch) runs 178 us per four owners with it against
-// 190 us without, while the 72 MB write-mode share slows from 9.9 to 13.7 us.
+// NT: non-temporal (streaming) load.  It keeps the data out of the 256 MB
+// MALL, which costs when the data would have stayed there: measured on
+// MI355X with grid-stride batches, the 4 x 64 Mi-element two-shot (268 MB per
+// launch) runs 178 us per four owners with it against 190 us without, while
+// the 72 MB write-mode share back to back on one buffer set slows from 9.9 to
+// 13.7 us.  The batch and pipelined kernels therefore take it only past
+// 128 MiB per launch; the one-pass phased kernel, tuned for data coming from
+// HBM, always does.
 template <bool NT>
 __device__ __forceinline__ u32x4 load_vec(const void *base, int64_t elem) {
     const u32x4 *p = reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(base) + elem);
@@ -94,8 +98,9 @@ __device__ __forceinline__ u32x4 load_vec(const void *base, int64_t elem) {
 // 15.57 instead of 15.72 us from HBM; two-shot rank 3 of 680x5120 x 8 3.20
 // instead of 3.35 us.  (SC1 without NT: 9.30 us warm but 17.4 us from HBM;
 // no policy bits: 17.7 against 14.4 us from HBM.)  WT = false stores with NT
-// alone: the one-pass kernel that issues four vectors per lane per input
-// before storing any runs better without the write-through (below).
+// alone: the one-pass kernels that issue all their loads before storing any
+// run better without the write-through (12.0 against 12.2 us for the phased
+// write-mode share from HBM).
 //
 // The store goes through a buffer resource so the policy can be chosen:
 // `base` must be the same for every lane of the wavefront (a kernel argument)
