@@ -143,9 +143,15 @@ __global__ __launch_bounds__(kThreads) void k_ll_encode(CodecArgs a) {
 }
 
 // Four words in flight per lane: 8-byte loads need many requests outstanding
-// to keep HBM busy.
+// to keep HBM busy.  A word whose two elements both lie in a 4-byte-aligned
+// destination is stored with one non-temporal 4-byte store; the rest go
+// through store_pair.  (Measured on MI355X for 512x7168: 3.40-3.48 us per
+// call back to back on one buffer pair against 3.75 us with store_pair for
+// every word, 5.69-5.74 against 5.85 us from HBM.)
 __global__ __launch_bounds__(kThreads) void k_ll_decode(CodecArgs a) {
     constexpr int K = 4;
+    const int64_t nwhole = a.aligned4 ? a.n / 2 : 0;  // words with both elements
+    uint32_t *dst32 = reinterpret_cast<uint32_t *>(a.elems);
     const int64_t stride = (int64_t)gridDim.x * kThreads;
     for (int64_t w0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; w0 < a.nwords;
          w0 += stride * K) {
@@ -162,7 +168,10 @@ __global__ __launch_bounds__(kThreads) void k_ll_decode(CodecArgs a) {
             if (word_flag(v[k]) != a.flag &&
                 !wait_word(a.words + w, a.flag, v[k], a.status, a.max_spins))
                 return;
-            store_pair(a.elems, 2 * w, a.n, a.aligned4, word_data(v[k]));
+            if (w < nwhole)
+                __builtin_nontemporal_store(word_data(v[k]), dst32 + w);
+            else
+                store_pair(a.elems, 2 * w, a.n, a.aligned4, word_data(v[k]));
         }
     }
 }
