@@ -18,6 +18,13 @@
 // a call share one 16-byte alignment the ragged head and tail take scalar
 // accesses and the bulk takes vectors; otherwise the whole range is scalar.
 // No LDS, no MFMA: there is no reuse to stage and no contraction.
+//
+// Three schedules of those loads and stores, chosen by size in launch_piece:
+// grid-stride batches (k_reduce) for the latency-bound sizes; one pass in
+// which every wave issues all its loads before any store, at most one wave
+// per SIMD (k_reduce_phased), which puts the device's reads first and its
+// writes last; and a two-stage software pipeline (k_reduce_pipe) in between
+// and beyond.
 #include "device.h"
 #include "host.h"
 

@@ -76,10 +76,22 @@ PACKET_SOURCES = ["allreduce_reduction_way_amd/csrc/device.h",
 COPY_PROBE_BYTES = 256 << 20
 
 
+def code_of(text: str) -> str:
+    """A C++ source with its comments removed and its white space collapsed:
+    what the compiler sees.  Comments in these sources hold no string
+    literals with comment markers, so a plain scan suffices."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(sources=None) -> str:
+    """Hash of the code (not the comments) of the sources a kernel is built
+    from: counters recorded for one hash describe every build with it."""
     h = hashlib.sha256()
     for rel in sources or KERNEL_SOURCES:
-        h.update((ROOT / rel).read_bytes())
+        h.update(code_of((ROOT / rel).read_text()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 

@@ -28,6 +28,15 @@ def test_traffic_is_reported_only_for_the_profiled_sources(monkeypatch):
     assert bench.traffic_from_profiles("write_bcast_440x5120_p8", 72089600) is None
 
 
+def test_source_hash_ignores_comments_but_not_code():
+    src = "int f(int a) {  // the answer\n    return a + 1; /* one more */\n}\n"
+    reworded = "// a new header line\nint f(int a) {\n  return a + 1;  // still one more\n}\n"
+    changed = "int f(int a) {  // the answer\n    return a + 2; /* one more */\n}\n"
+    assert bench.code_of(src) == bench.code_of(reworded)
+    assert bench.code_of(src) != bench.code_of(changed)
+    assert "answer" not in bench.code_of(src) and "return a + 1;" in bench.code_of(src)
+
+
 def test_packet_byte_accounting():
     n = 512 * 7168
     # P = 8: read 2n + 2 * 3.5n, write 10n  ->  19n per rank
