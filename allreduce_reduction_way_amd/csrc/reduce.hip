@@ -364,8 +364,9 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
     //    x 4 (one owner of the 64 Mi two-shot) 47.9 against 51.0 us for 256-lane
     //    grid-stride batches, x 8 103.4 against 110.2 us, x 6 72.1 against 78.2.
     // With the data in the MALL instead (back-to-back calls on one buffer set
-    // of up to 256 MB) grid-stride batches are faster (9.4 against 11.2 us for
-    // the 440x5120 x 8 share); the automatic choice is made for data from HBM.
+    // of up to 256 MB) the pipelined kernel is faster (9.0 against 10.1-11.1 us
+    // for the 440x5120 x 8 share); the automatic choice is made for data from
+    // HBM.
     int threads = 64, U = 1, sched = kBatch;
     int64_t blocks = 0;  // 0: the grid covers the bulk (set below)
     const int64_t vpc = (a.nvec + dev.cus - 1) / dev.cus;
