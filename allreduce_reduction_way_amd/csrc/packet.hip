@@ -85,7 +85,7 @@ __device__ __forceinline__ void store_pair(uint16_t *p, int64_t e, int64_t len, 
 // kernel-argument loads at the start of every wave.  Measured on MI355X, the
 // encode of 512x7168 from HBM: 5.25 against 5.65 us per call.
 struct CodecArgs {
-    uint16_t *elems;        // encode: source (only read); decode: destination
+    uint16_t *elems;        // decode destination
     uint64_t *words;        // packet words (2 per packet)
     int64_t n;
     int64_t nwords;
@@ -96,50 +96,89 @@ struct CodecArgs {
 };
 static_assert(sizeof(CodecArgs) <= 56, "the grid size must share the arguments' first 64-byte line");
 
-// Encode.  The bulk -- the words whose two elements both lie in a 4-byte
-// aligned source -- goes kEncodeUnroll words per lane in one pass: global
+// One encode launch: word w of `words` packs elements 2w and 2w+1 of
+// `elems`.  Words [0, nbulk) are the bulk (both elements exist, `elems` is
+// 4-byte aligned); words [nbulk, nwords) take one word per lane.
+struct EncodeArgs {
+    const uint16_t *elems;
+    uint64_t *words;
+    int64_t n;       // elements from `elems`
+    int64_t nbulk;
+    int64_t nwords;
+    uint32_t flag;
+};
+static_assert(sizeof(EncodeArgs) <= 56, "the grid size must share the arguments' first 64-byte line");
+
+// Encode.  The bulk goes kEncodeUnroll words per lane in one pass: global
 // wave g takes the kEncodeUnroll x 64 consecutive words from
-// g x kEncodeUnroll x 64 (and the same again one grid further on while the
-// bulk lasts) and issues all its loads before any store (the
+// g x kEncodeUnroll x 64 and issues all its loads before any store (the
 // scheduling barrier keeps them apart), so the device sees mostly reads,
 // then mostly writes.  Lanes past the bulk load its last word again (in
-// bounds) and store nothing.  The rest -- the odd last element, the zero
-// padding of the last packet, or the whole range for a 2-byte-aligned source
-// -- takes one word per lane.  Measured on MI355X for 512x7168 with the
-// data in HBM (32 buffer pairs in turn): 5.25 us per call against 5.99 us for
-// one word per lane in a grid stride; back to back on one buffer pair 4.12
-// against 4.02 us.
+// bounds) and give their stores an offset past the resource's range, which
+// the hardware drops: no branch around the stores.  The stores are the
+// 8-byte device-scope (sc1) stores of an agent-scope atomic plus the
+// streaming hint (nt), through one buffer resource per launch; a range
+// longer than kEncodePieceWords runs as several launches so every offset
+// fits the resource.  The rest -- the odd last element, the zero padding of
+// the last packet, or the whole range for a 2-byte-aligned source -- takes
+// one word per lane in a grid stride.  Measured on MI355X for 512x7168, in
+// one process: from HBM (32 buffer pairs in turn) 4.8 us per call against
+// 5.3 us for the same loads with per-lane agent-scope atomic stores behind
+// bounds branches in a grid-stride loop; back to back on one buffer pair
+// about 3.5-3.6 us for both.
 constexpr int kEncodeUnroll = 4;
-// Grid cap of the encode: 2^20 workgroups of 256 lanes keep the launch's
-// work-item count (a 32-bit field of the dispatch packet) far from overflow.
-constexpr int64_t kMaxEncodeBlocks = 1ll << 20;
+constexpr int64_t kEncodePieceWords = 1ll << 27;
+static_assert(8 * kEncodePieceWords + 8 <= (int64_t)kStoreRangeBytes,
+              "every packet word of an encode piece must lie inside the store range");
 
-__global__ __launch_bounds__(kThreads) void k_ll_encode(CodecArgs a) {
-    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t nbulk = a.aligned4 ? a.n / 2 : 0;
-    constexpr int U = kEncodeUnroll;
-    const int64_t nwaves = (int64_t)gridDim.x * (kThreads / 64);
-    // one pass when the grid covers the bulk; larger ranges loop by waves
-    for (int64_t c = g >> 6; c * 64 * U < nbulk; c += nwaves) {
-        const int64_t base = c * (64 * U) + (g & 63);
-        const uint32_t *src = reinterpret_cast<const uint32_t *>(a.elems);
-        uint32_t d[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int64_t w = base + 64 * u;
-            w = w < nbulk ? w : nbulk - 1;
-            d[u] = __builtin_nontemporal_load(src + w);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t w = base + 64 * u;
-            if (w < nbulk) store_word(a.words + w, make_word(d[u], a.flag));
-        }
-    }
+// The 8-byte store of an agent-scope atomic (sc1: through to the device
+// coherence point) with the streaming hint (nt), at byte offset `byte_off`
+// from `base` (the same for every lane of the wavefront); dropped past
+// kStoreRangeBytes.
+__device__ __forceinline__ void store_word_stream(uint64_t *base, uint32_t byte_off, uint64_t w) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(base, (short)0, kStoreRangeBytes, 0x00020000);
+    u32x2 v;
+    v[0] = word_data(w);
+    v[1] = word_flag(w);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, byte_off, 0, 18);
+}
+
+// Words [from, nwords), one per lane, grid stride.
+__device__ __forceinline__ void encode_words(const EncodeArgs &a, int64_t from) {
     const int64_t stride = (int64_t)gridDim.x * kThreads;
-    for (int64_t w = nbulk + g; w < a.nwords; w += stride)
+    for (int64_t w = from + (int64_t)blockIdx.x * kThreads + threadIdx.x; w < a.nwords;
+         w += stride)
         store_word(a.words + w, make_word(load_pair(a.elems, 2 * w, a.n, false), a.flag));
+}
+
+// The bulk (nbulk >= 1, one pass: the grid covers it), then the tail.
+__global__ __launch_bounds__(kThreads) void k_ll_encode(EncodeArgs a) {
+    constexpr int U = kEncodeUnroll;
+    const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t base = (g >> 6) * (64 * U) + (g & 63);
+    const uint32_t *src = reinterpret_cast<const uint32_t *>(a.elems);
+    uint32_t d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        int64_t w = base + 64 * u;
+        w = w < a.nbulk ? w : a.nbulk - 1;
+        d[u] = __builtin_nontemporal_load(src + w);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t w = base + 64 * u;
+        const uint32_t off = w < a.nbulk ? (uint32_t)(8 * w) : kDroppedStoreOffset;
+        store_word_stream(a.words, off, make_word(d[u], a.flag));
+    }
+    encode_words(a, a.nbulk);
+}
+
+// No bulk: every word one per lane.
+__global__ __launch_bounds__(kThreads) void k_ll_encode_words(EncodeArgs a) {
+    encode_words(a, 0);
 }
 
 // Four words in flight per lane: 8-byte loads need many requests outstanding
@@ -655,25 +694,31 @@ int ar_ll_encode(const void *src, void *dst_pkts, int64_t n, uint32_t flag, void
         return AR_EALIAS;
     DeviceInfo dev;
     if (current_device(&dev) != AR_OK) return AR_ELAUNCH;
-    CodecArgs a = {};
-    a.elems = static_cast<uint16_t *>(const_cast<void *>(src));  // only read
-    a.words = static_cast<uint64_t *>(dst_pkts);
-    a.n = n;
-    a.nwords = 2 * ar_ll_packets(n);
-    a.flag = flag;
-    a.aligned4 = aligned_to(src, 4);
-    // the bulk takes one pass (see k_ll_encode); without one, a grid stride
-    // of at most 8 workgroups per CU over every word
-    const int64_t nbulk = a.aligned4 ? n / 2 : 0;
-    const int64_t per_block = (int64_t)kThreads * kEncodeUnroll;
-    int64_t blocks = (nbulk + per_block - 1) / per_block;
-    if (blocks > kMaxEncodeBlocks) blocks = kMaxEncodeBlocks;  // the kernel loops beyond
+    const uint16_t *elems = static_cast<const uint16_t *>(src);
+    uint64_t *words = static_cast<uint64_t *>(dst_pkts);
+    const int64_t nwords = 2 * ar_ll_packets(n);
+    const int64_t nbulk = aligned_to(src, 4) ? n / 2 : 0;
     if (nbulk == 0) {
-        blocks = (a.nwords + kThreads - 1) / kThreads;
+        // a grid stride of at most 8 workgroups per CU over every word
+        EncodeArgs a = {elems, words, n, 0, nwords, flag};
+        int64_t blocks = (nwords + kThreads - 1) / kThreads;
         if (blocks > (int64_t)dev.cus * 8) blocks = (int64_t)dev.cus * 8;
+        return launch(reinterpret_cast<const void *>(&k_ll_encode_words), (unsigned)blocks,
+                      kThreads, a, stream);
     }
-    return launch(reinterpret_cast<const void *>(&k_ll_encode), (unsigned)blocks, kThreads, a,
-                  stream);
+    // the bulk in pieces of at most kEncodePieceWords words, one pass each;
+    // the last piece also takes the tail
+    const int64_t per_block = (int64_t)kThreads * kEncodeUnroll;
+    for (int64_t w0 = 0; w0 < nbulk; w0 += kEncodePieceWords) {
+        const int64_t piece = nbulk - w0 < kEncodePieceWords ? nbulk - w0 : kEncodePieceWords;
+        const bool last = w0 + piece == nbulk;
+        EncodeArgs a = {elems + 2 * w0, words + w0, n - 2 * w0, piece,
+                        last ? nwords - w0 : piece, flag};
+        const int rc = launch(reinterpret_cast<const void *>(&k_ll_encode),
+                              (unsigned)((piece + per_block - 1) / per_block), kThreads, a, stream);
+        if (rc != AR_OK) return rc;
+    }
+    return AR_OK;
 }
 
 int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void *ctrl,

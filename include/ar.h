@@ -146,8 +146,10 @@ int ar_reduce_scatter_share(ar_ptrs in, void *out, int P, int rank, int64_t recv
  *     word 2 = elem[4k+2] | elem[4k+3] << 16      (data1)
  *     word 3 = flag                               (flag1)
  * Elements past n are encoded as 0.  Each 8-byte half {data, flag} is written
- * and read as one agent-scope atomic, so a reader that sees the expected flag
- * in a half also sees that half's data.  A packet counts as arrived only when
+ * with one 8-byte device-scope store (the store of an agent-scope atomic; the
+ * standalone encode adds the streaming hint) and read as one agent-scope
+ * atomic, so a reader that sees the expected flag in a half also sees that
+ * half's data.  A packet counts as arrived only when
  * both flags equal the expected value; flags are never cleared, so a packet
  * left by an earlier call (older flag) reads as not yet arrived (torchcomms
  * PR #3850, commit summary D117629704: flags never cleared, stale flags
