@@ -343,15 +343,21 @@ def test_packet_fused_two_byte_aligned_buffers(in_shift, out_shift):
 
 
 @pytest.mark.parametrize("n", [1, 2, 5, 4096 * 3 + 3])
-def test_ll_encode_from_two_byte_aligned_source(n):
+@pytest.mark.parametrize("shift", [1, 2])
+def test_ll_encode_from_two_or_four_byte_aligned_source(n, shift):
+    """shift 1: a 2-byte-aligned source (one word per lane throughout);
+    shift 2: 4-byte but not 8-byte aligned (the bulk path)."""
     rng = np.random.default_rng(n + 99)
     y = rng.integers(0, 1 << 16, n, dtype=np.uint32).astype(np.uint16)
-    src = Guarded(n, shift=1, init=y)
-    pk = torch.zeros(16 * O.ll_packets(n), dtype=torch.uint8, device=DEV)
-    announce(f"ll_encode from a 2-byte-aligned source n={n}")
+    src = Guarded(n, shift=shift, init=y)
+    pk = torch.zeros(16 * O.ll_packets(n) + 64, dtype=torch.uint8, device=DEV)
+    announce(f"ll_encode from a source at element offset {shift} n={n}")
     ar.ar_ll_encode(src.view, pk, 77)
     torch.cuda.synchronize()
-    assert np.array_equal(pk.cpu().numpy().view(np.uint32), O.ll_encode(y, 77))
+    got = pk.cpu().numpy()
+    assert got[16 * O.ll_packets(n):].sum() == 0          # nothing past the last packet
+    assert np.array_equal(got[: 16 * O.ll_packets(n)].view(np.uint32), O.ll_encode(y, 77))
+    assert src.guards_intact()
 
 
 @pytest.mark.parametrize("in_shift,out_shift", [(0, 0), (2, 0), (0, 2), (1, 3), (2, 2)])
