@@ -82,8 +82,9 @@ __device__ __forceinline__ void store_pair(uint16_t *p, int64_t e, int64_t len, 
 // 56 bytes, so that the grid size the runtime appends after them (read for
 // the grid strides) shares their first 64-byte line: with a 64-byte struct it
 // fell on a second line, whose fetch came as a second dependent round of
-// kernel-argument loads at the start of every wave.  Measured on MI355X, the
-// encode of 512x7168 from HBM: 5.25 against 5.65 us per call.
+// kernel-argument loads at the start of every wave.  Measured on MI355X with
+// an LL encode kernel on this struct, 512x7168 from HBM: 5.25 against 5.65 us
+// per call.  The encode's own arguments (EncodeArgs) keep the same bound.
 struct CodecArgs {
     uint16_t *elems;        // decode destination
     uint64_t *words;        // packet words (2 per packet)
@@ -125,7 +126,7 @@ static_assert(sizeof(EncodeArgs) <= 56, "the grid size must share the arguments'
 // one process: from HBM (32 buffer pairs in turn) 4.8 us per call against
 // 5.3 us for the same loads with per-lane agent-scope atomic stores behind
 // bounds branches in a grid-stride loop; back to back on one buffer pair
-// about 3.5-3.6 us for both.
+// 3.37 against 3.63 us.
 constexpr int kEncodeUnroll = 4;
 constexpr int64_t kEncodePieceWords = 1ll << 27;
 static_assert(8 * kEncodePieceWords + 8 <= (int64_t)kStoreRangeBytes,
