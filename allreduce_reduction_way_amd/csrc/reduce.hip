@@ -359,10 +359,18 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
     //    keeps U = 4 up to vpc 1536 (x 4 at 1536: 8.7 us against 9.3 with
     //    U = 6), then one wave per SIMD up to U = 8 (x 4 at 2560: 14.1 us
     //    against 16.0 with U = 4);
-    //  - beyond: the two-stage pipelined kernel in 64-lane workgroups, one
-    //    vector per lane per stage, a grid that covers the bulk: 16M elements
-    //    x 4 (one owner of the 64 Mi two-shot) 47.9 against 51.0 us for 256-lane
-    //    grid-stride batches, x 8 103.4 against 110.2 us, x 6 72.1 against 78.2.
+    //  - beyond, with P outputs (write mode, two-shot): the two-stage
+    //    pipelined kernel in 64-lane workgroups, one vector per lane per stage,
+    //    a grid that covers the bulk: 16M elements x 4 (one owner of the 64 Mi
+    //    two-shot) 47.9 against 51.0 us for 256-lane grid-stride batches, x 8
+    //    103.4 against 110.2 us, x 6 72.1 against 78.2;
+    //  - beyond, with one output (one-shot, reduce-scatter): one pass with
+    //    U = 2 and a grid that covers the bulk, several waves per SIMD.  Median
+    //    of 9 for 8M / 16M / 32M elements: x 8 26.9 / 49.7 / 97.1 us against
+    //    27.5 / 51.9 / 100.1 for the pipelined kernel, x 4 15.7 / 28.8 / 54.5
+    //    against 16.2 / 28.8 / 54.9, x 2 10.1 / 17.4 / 31.7 against 10.3 /
+    //    18.4 / 32.7 (U = 3 or 4 won some of these by up to 6% and lost the
+    //    32M ones by up to 3%).
     // With the data in the MALL instead (back-to-back calls on one buffer set
     // of up to 256 MB) the pipelined kernel is faster (9.0 against 10.1-11.1 us
     // for the 440x5120 x 8 share); the automatic choice is made for data from
@@ -382,6 +390,9 @@ int launch_piece(const ar_ptrs &in_at, const ar_ptrs &out_at, int P, bool bcast,
                                                           : (P == 8 ? 5 : phased_max_unroll(P));
         else
             U = vpc <= 1536 ? 4 : (one_wave_per_simd < 8 ? one_wave_per_simd : 8);
+    } else if (!bcast) {
+        sched = kPhased;
+        U = 2;
     } else {
         sched = kPipe2;
     }

@@ -117,3 +117,36 @@ def test_automatic_shape_classes(P, n):
         for o in outs:
             assert np.array_equal(o.host(), y)
             assert o.guards_intact()
+
+
+# With one output (one-shot sum, reduce-scatter) the rule takes the phased
+# kernel with two vectors per lane beyond 2560 bulk vectors per CU; sizes on
+# both sides of every switch, aligned and misaligned.
+@pytest.mark.parametrize("P,n", [(8, 524_288 + 9), (4, 1_572_864 + 11), (8, 5_242_880 - 7),
+                                 (8, 5_242_880 + 5), (2, 5_242_880 + 5), (4, 8_388_608 + 3)])
+def test_automatic_shape_classes_one_output(P, n):
+    ar.ar_set_reduce_tuning(0, 0, 0, 0)
+    for shift in (0, 5):
+        xs = I.make_inputs("uniform", P, n, seed=P * 11 + shift)
+        y = O.oneshot_sum(xs)
+        ins = [Guarded(n, shift=shift, init=x) for x in xs]
+        out = Guarded(n, shift=shift)
+        announce(f"automatic shape oneshot_sum P={P} n={n} shift={shift}")
+        ar.ar_oneshot_sum([g.view for g in ins], out.view)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.host(), y)
+        assert out.guards_intact()
+
+
+def test_automatic_reduce_scatter_past_2560_vectors_per_cu():
+    P, rc = 2, 5_242_880 + 13
+    xs = I.make_inputs("uniform", P, P * rc, seed=17)
+    rs_in = [to_dev(x) for x in xs]
+    ar.ar_set_reduce_tuning(0, 0, 0, 0)
+    for rank in (0, 1):
+        out = Guarded(rc)
+        announce(f"automatic shape reduce-scatter P={P} recvcount={rc} rank={rank}")
+        ar.ar_reduce_scatter_share(rs_in, out.view, rank)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.host(), O.reduce_scatter(xs, rank))
+        assert out.guards_intact()
