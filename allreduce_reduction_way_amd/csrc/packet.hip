@@ -188,30 +188,6 @@ __global__ __launch_bounds__(kThreads) void k_ll_encode_words(EncodeArgs a) {
 // through store_pair.  (Measured on MI355X for 512x7168: 3.40-3.48 us per
 // call back to back on one buffer pair against 3.75 us with store_pair for
 // every word, 5.69-5.74 against 5.85 us from HBM.)
-//
-// The first read of each word is the 8-byte load of an agent-scope atomic
-// (sc1) with the streaming hint (nt), through one buffer resource per launch;
-// a word whose flag has not arrived is then polled with load_word.  Measured
-// on MI355X for 512x7168, in one process: 5.43-5.46 against 5.68 us per call
-// from HBM (32 packet buffers in turn) for the atomic load, 3.40-3.51 against
-// 3.48-3.67 us back to back; sc1 alone through the resource 5.61 us.  The
-// compiler issues the K loads, waits for all of them, then checks and stores
-// word by word; unconditional loads, which it waited for one at a time with
-// each word stored as soon as its own load landed, ran 6.08 us from HBM.  A
-// range longer than kDecodePieceWords runs as several launches so every
-// offset fits the resource.
-constexpr int64_t kDecodePieceWords = 1ll << 27;
-static_assert(8 * kDecodePieceWords + 8 <= (int64_t)kStoreRangeBytes,
-              "every packet word of a decode piece must lie inside the buffer range");
-
-__device__ __forceinline__ uint64_t load_word_stream(const uint64_t *base, uint32_t byte_off) {
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint64_t *>(base), (short)0, kStoreRangeBytes, 0x00020000);
-    const u32x2 q = __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 18);
-    return make_word(q[0], q[1]);
-}
-
 __global__ __launch_bounds__(kThreads) void k_ll_decode(CodecArgs a) {
     constexpr int K = 4;
     const int64_t nwhole = a.aligned4 ? a.n / 2 : 0;  // words with both elements
@@ -223,8 +199,7 @@ __global__ __launch_bounds__(kThreads) void k_ll_decode(CodecArgs a) {
 #pragma unroll
         for (int k = 0; k < K; ++k) {
             const int64_t w = w0 + k * stride;
-            v[k] = w < a.nwords ? load_word_stream(a.words, (uint32_t)(8 * w))
-                                : make_word(0, a.flag);
+            v[k] = w < a.nwords ? load_word(a.words + w) : make_word(0, a.flag);
         }
 #pragma unroll
         for (int k = 0; k < K; ++k) {
@@ -777,23 +752,10 @@ int ar_ll_decode(const void *src_pkts, void *dst, int64_t n, uint32_t flag, void
     if (per_cu <= 0) return AR_ELAUNCH;
     int64_t cap = (int64_t)per_cu * dev.cus / 2;
     if (cap < 1) cap = 1;
-    // pieces of at most kDecodePieceWords words; all but the last hold whole
-    // words only, so each piece's element count is twice its word count
-    for (int64_t w0 = 0; w0 < a.nwords; w0 += kDecodePieceWords) {
-        const int64_t piece =
-            a.nwords - w0 < kDecodePieceWords ? a.nwords - w0 : kDecodePieceWords;
-        CodecArgs b = a;
-        b.elems = a.elems + 2 * w0;
-        b.words = a.words + w0;
-        b.n = w0 + piece == a.nwords ? n - 2 * w0 : 2 * piece;
-        b.nwords = piece;
-        int64_t blocks = (piece + 4 * kThreads - 1) / (4 * kThreads);
-        if (blocks > cap) blocks = cap;
-        const int rc = launch(reinterpret_cast<const void *>(&k_ll_decode), (unsigned)blocks,
-                              kThreads, b, stream);
-        if (rc != AR_OK) return rc;
-    }
-    return AR_OK;
+    int64_t blocks = (a.nwords + 4 * kThreads - 1) / (4 * kThreads);
+    if (blocks > cap) blocks = cap;
+    return launch(reinterpret_cast<const void *>(&k_ll_decode), (unsigned)blocks, kThreads, a,
+                  stream);
 }
 
 int ar_packet_fused(ar_ptrs in, ar_ptrs scratch, ar_ptrs out, int P, int rank_lo, int rank_hi,
