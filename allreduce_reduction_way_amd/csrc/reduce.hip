@@ -21,10 +21,11 @@
 //
 // Three schedules of those loads and stores, chosen by size in launch_piece:
 // grid-stride batches (k_reduce) for the latency-bound sizes; one pass in
-// which every wave issues all its loads before any store, at most one wave
-// per SIMD (k_reduce_phased), which puts the device's reads first and its
-// writes last; and a two-stage software pipeline (k_reduce_pipe) in between
-// and beyond.
+// which every wave issues all its loads before any store (k_reduce_phased),
+// at most one wave per SIMD in the middle range, which puts the device's
+// reads first and its writes last, and several per SIMD for the largest
+// one-output calls; and a two-stage software pipeline (k_reduce_pipe) just
+// above the latency-bound sizes and for the largest calls with P outputs.
 #include "device.h"
 #include "host.h"
 
