@@ -634,8 +634,14 @@ int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const a
     }
 
     // Persistent grid no larger than what is resident at once: B workgroups per
-    // rank, then B rebalanced so that every workgroup runs the same number of
-    // chunks.
+    // rank, every one that fits.  Only when that leaves at most two chunks per
+    // workgroup is B lowered so that every workgroup runs the same number.
+    // Measured on MI355X in one process (medians of 7, P x n): keeping every
+    // resident workgroup ran 8 x 3.67M in 96.8-97.4 against 100.3-101.5 us
+    // for the evened grid, 8 x 2M 55.9 against 58.7, 8 x 2.6M 71.5 against
+    // 75.3, 8 x 6M 169.5 against 175.0, 8 x 12M 341.4 against 356.4, 4 x 3.67M
+    // 48.1 against 51.8; with two chunks per workgroup at most the evened
+    // grid won (8 x 1M: 32.2 against 34.3 us) or tied (8 x 1.5M).
     const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(fn));
     if (per_cu <= 0) return AR_ELAUNCH;
     const int64_t resident = (int64_t)per_cu * dev.cus;
@@ -646,7 +652,7 @@ int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const a
     if (B > a.chunks) B = a.chunks;
     if (B < 1) return AR_ELAUNCH;
     const int64_t rounds = (a.chunks + B - 1) / B;
-    B = (a.chunks + rounds - 1) / rounds;
+    if (rounds <= 2) B = (a.chunks + rounds - 1) / rounds;
     a.per_rank = (int)B;
     return launch(reinterpret_cast<const void *>(fn), (unsigned)(roles * B * a.nranks), kThreads,
                   a, stream);
