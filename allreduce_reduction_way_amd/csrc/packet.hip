@@ -640,8 +640,10 @@ int packet_call(Kind kind_in, const ar_ptrs &in, const ar_ptrs &scratch, const a
     // resident workgroup ran 8 x 3.67M in 96.8-97.4 against 100.3-101.5 us
     // for the evened grid, 8 x 2M 55.9 against 58.7, 8 x 2.6M 71.5 against
     // 75.3, 8 x 6M 169.5 against 175.0, 8 x 12M 341.4 against 356.4, 4 x 3.67M
-    // 48.1 against 51.8; with two chunks per workgroup at most the evened
-    // grid won (8 x 1M: 32.2 against 34.3 us) or tied (8 x 1.5M).
+    // 48.1 against 51.8, 6 x 3.67M 73.5 against 82.4, 5 x 3.67M 62.2 against
+    // 66.7, 3 x 3.67M 35.8 against 38.4; with two chunks per workgroup at most
+    // the evened grid won (8 x 1M: 32.2 against 34.3 us) or tied (8 x 1.5M,
+    // 6 x 1.5M, 8 x 0.8M).
     const int per_cu = blocks_per_cu(dev, reinterpret_cast<const void *>(fn));
     if (per_cu <= 0) return AR_ELAUNCH;
     const int64_t resident = (int64_t)per_cu * dev.cus;
